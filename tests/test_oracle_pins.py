@@ -1,0 +1,9 @@
+"""The fp64 oracle against the pins in ``pins.py`` (CPU only)."""
+import pytest
+
+from tests import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin, oracle_lib):
+    pin(oracle_lib)
