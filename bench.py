@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+One step = one call of the whole forward pass (one kernel launch of fa_fwd)
+over one batch of seeded synthetic input that is already resident in HBM.
+Default workload: B=2, H=32, N=8192, d=128, bf16, causal (the configuration
+the MFMA-peak target is stated for).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+FLOPs are the nominal matmul count 4*B*H*N^2*d, halved under the causal
+mask.  `roofline` reports the kernel's own average launch duration, measured
+with HIP events recorded on the launch stream, against the bf16 dense MFMA
+peak; `traffic` comes from the committed rocprofv3 counter summary of the
+same command when it still matches the kernel source.  `cpu_baseline` times
+the fp64 oracle on a bounded sample of rows of the same workload.
+
+Counter helpers (used to produce the summaries under profiles/):
+  python bench.py --copy-calibration ...   also runs one plain device copy
+                                           of 1 GiB (for counter scaling)
+  python bench.py --summarize-counters DIR  turn rocprofv3 --pmc output
+                                           into the text summary
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU * 2.4 GHz * 4096 FLOP/clk
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (used only for fp32 workloads)
+KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_fwd_bf16.hip",
+                  "exact_attention_32_amd/csrc/fa_fwd_f32.hip"]
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = "profiles/fa_fwd_bf16_b2h32n8192d128_causal_traffic.txt"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """Bytes per launch from the committed counter summary, or None when the
+    summary is for another workload or an older kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].isupper():
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("WORKLOAD") != workload:
+        return None
+    if fields.get("KERNEL_SOURCE_SHA256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["HBM_BYTES_PER_LAUNCH"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """The oracle as it stands, timed on the host cores on a seeded sample of
+    output rows of the same workload; nominal FLOPs per row are the
+    workload's FLOPs divided by its number of rows."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_32_amd import inputs
+
+    o = oracle.default()
+    qd, kd, vd = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+    per_row = w.flops / (w.B * w.H * w.N)
+    # calibrate on a few rows, then size the sample to about target_s seconds
+    rows = inputs.sample_rows(w, 64, seed=99)
+    t0 = time.perf_counter()
+    o.attention_rows(qd, kd, vd, w.scale, w.causal, rows)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(200000, max(64, 64 * target_s / dt)))
+    rows = inputs.sample_rows(w, n, seed=100)
+    t0 = time.perf_counter()
+    o.attention_rows(qd, kd, vd, w.scale, w.causal, rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n * per_row / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} seeded output rows of {w.name} (fp64 definition, full score row "
+                  f"each), {dt:.1f} s; FLOPs per row = workload FLOPs / rows",
+    }
+
+
+def summarize_counters(directory: str) -> None:
+    """Print the traffic summary from two rocprofv3 --pmc runs (one with
+    FETCH_SIZE, one with WRITE_SIZE, both of `bench.py --copy-calibration`)
+    found under `directory`."""
+    import csv
+
+    per_counter = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        for row in csv.DictReader(open(path)):
+            name = row.get("Counter_Name") or row.get("Counter-Name")
+            kern = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
+            val = float(row.get("Counter_Value") or row.get("Counter-Value"))
+            disp = row.get("Dispatch_Id") or row.get("Dispatch-Id")
+            per_counter.setdefault(name, {}).setdefault((kern, disp), 0.0)
+            per_counter[name][(kern, disp)] += val
+    out = {}
+    for name, d in per_counter.items():
+        fa_vals = [v for (kern, _), v in d.items() if "fwd_bf16_kernel" in kern]
+        cp_vals = [v for (kern, _), v in d.items()
+                   if "fwd_" not in kern and v * 1024 > COPY_BYTES / 4]
+        out[name] = (fa_vals, cp_vals)
+    for name, (fa_vals, cp_vals) in out.items():
+        print(f"{name}: fa launches={len(fa_vals)} mean={sum(fa_vals)/max(1,len(fa_vals)):.1f} KiB;"
+              f" copy kernels={len(cp_vals)} values={cp_vals}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: this build measures one GPU only (single-GPU kernel, no "
+                  "collectives); run it with --gpus 1.", flush=True)
+        return 2
+
+    import torch
+
+    import exact_attention_32_amd as fa
+    from exact_attention_32_amd import inputs
+
+    name = args.workload or inputs.HEADLINE
+    w = inputs.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_qkv(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)   # default priority
+    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+
+    def step():
+        rc = fn(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, stream)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, fa.fa_strerror(rc))
+
+    torch.cuda.synchronize(dev)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize(dev)
+
+    # Timed region: K steps, synchronised on both sides.  Per-launch event
+    # pairs on the launch stream give the kernel's average duration.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            step()
+            b.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    ms_per_step = wall * 1e3 / args.steps
+
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    line = {
+        "metric": "attention fwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "inputs": w.dist, "flops_per_step": w.flops,
+                   "pct_mfma_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": read_traffic(w.name),
+                     "kernel_ms": round(kernel_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,26 @@
-"""MI355X-native exact attention forward pass (package under construction)."""
+"""MI355X (gfx950) exact attention forward pass.
+
+O = softmax(scale * Q K^T [+ causal mask]) V and the per-row log-sum-exp,
+computed tile by tile in hand-written HIP kernels behind the C ABI of
+``include/fa.h``.  This package is the thin Python binding of that library
+(``fa_fwd``, ``fa_fwd_f32``, ``fa_strerror`` with the C names, plus the torch
+convenience ``forward``) and the seeded input generators in ``inputs``.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    FA_ERR_ALIAS,
+    FA_ERR_ALIGN,
+    FA_ERR_HEADDIM,
+    FA_ERR_HIP,
+    FA_ERR_NULL,
+    FA_ERR_SCALE,
+    FA_ERR_SHAPE,
+    FA_OK,
+    LIB_PATH,
+    FAError,
+    fa_fwd,
+    fa_fwd_f32,
+    fa_strerror,
+    forward,
+    load_library,
+)

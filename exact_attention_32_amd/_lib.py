@@ -1,0 +1,122 @@
+"""ctypes binding of libfa (include/fa.h).  Argument marshalling only: every
+step of the computation runs in the HIP kernels of the library.
+
+There is no fallback: if ``libfa.so`` has not been built, or cannot be
+loaded, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEADDIM = 3
+FA_ERR_SCALE = 4
+FA_ERR_ALIGN = 5
+FA_ERR_HIP = 6
+FA_ERR_ALIAS = 7
+
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once; raise if it is missing (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m exact_attention_32_amd.build_lib` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("fa_fwd", "fa_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.restype = i
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_strerror.argtypes = [i]
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    return int(s)
+
+
+def fa_strerror(code: int) -> str:
+    return load_library().fa_strerror(int(code)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
+    """Enqueue the bf16 forward pass; pointers may be ints or tensors.
+    Returns the fa_status code (0 on success)."""
+    return int(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     int(B), int(H), int(N), int(d), float(scale),
+                                     int(bool(causal)), _stream(stream)))
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
+    """Enqueue the fp32 forward pass; same arguments as fa_fwd."""
+    return int(load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                         int(B), int(H), int(N), int(d), float(scale),
+                                         int(bool(causal)), _stream(stream)))
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            stream=None):
+    """Torch convenience wrapper: q, k, v are contiguous [B, H, N, d] device
+    tensors, all bf16 or all fp32.  Allocates O (input dtype) and LSE (fp32,
+    [B, H, N]) unless given, enqueues the kernel on ``stream`` (default: the
+    current torch stream) and returns (O, LSE).  ``scale`` defaults to
+    1/sqrt(d), the factor of the attention definition."""
+    import torch
+
+    if not (q.shape == k.shape == v.shape and q.dim() == 4):
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must all be bfloat16 or all be float32")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    rc = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return out, lse

@@ -1,0 +1,76 @@
+// fa_api.cpp -- the C ABI of libfa (declared in include/fa.h): argument
+// validation, kernel selection and launch.  Every check runs before anything
+// is enqueued; no HIP runtime call is made for an invalid argument list.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_internal.h"
+
+namespace {
+
+bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+
+int validate(const void *q, const void *k, const void *v, const void *o, const void *lse,
+             int B, int H, int N, int d, float scale, uint64_t elem_bytes) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    // B*H*N*d < 2^40, evaluated without overflow (N*d < 2^38, B*H < 2^62).
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
+    const uint64_t rows = bh * (uint64_t)N;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    for (const void *p : {q, k, v, o, lse})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    const uint64_t t_bytes = rows * (uint64_t)d * elem_bytes;
+    const uint64_t l_bytes = rows * 4u;
+    for (const void *in : {q, k, v}) {
+        if (overlaps(o, t_bytes, in, t_bytes)) return FA_ERR_ALIAS;
+        if (overlaps(lse, l_bytes, in, t_bytes)) return FA_ERR_ALIAS;
+    }
+    if (overlaps(o, t_bytes, lse, l_bytes)) return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+           int N, int d, float scale, int causal, hipStream_t stream) {
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2);
+    if (rc != FA_OK) return rc;
+    const hipError_t e =
+        fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B,
+               int H, int N, int d, float scale, int causal, hipStream_t stream) {
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 4);
+    if (rc != FA_OK) return rc;
+    const hipError_t e =
+        fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char *fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK: success";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: need B, H, N >= 1, N <= 2^30 and B*H*N*d < 2^40";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d must be 64 or 128";
+        case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";
+        case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o or lse overlaps an input or each other";
+        default: return "unknown fa status code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+/*
+ * fa.h -- C ABI of libfa, the MI355X (gfx950) exact attention forward pass.
+ *
+ *   O   = softmax(scale * Q K^T [+ causal mask]) V
+ *   LSE = log-sum-exp of each row of the scaled, masked logits (natural log)
+ *
+ * The operation is the one defined on the page "解析 FlashAttention（2）：
+ * FlashAttention-v1 前向传播" (section 1.1 for S = QK^T, P = softmax(S),
+ * O = PV; section 2.1, eq. (2)-(5) for the safe softmax; section 3.2 for the
+ * per-row output with its maximum m_i and sum l_i) and computed tile by tile
+ * with online softmax (same page, sections 2.5-3.12 and its Algorithm 1;
+ * loop order: query tiles outside, key/value tiles inside, as in the
+ * FlashAttention-2 loop of "在线 Softmax 与 FlashAttention", loop-order
+ * lesson).  The causal mask is the top-left one of that lesson's causal part:
+ * query i sees keys j <= i; tiles wholly in the future are skipped.
+ * The N x N score and probability matrices never reach device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout:    q, k, v, o are dense, contiguous [B, H, N, d] row-major tensors
+ *            (d fastest).  lse is a dense fp32 [B, H, N] tensor.  The query
+ *            and key sequences have the same length N.
+ * Memory:    every pointer is a device address the caller allocated (e.g. a
+ *            torch tensor on the current device) and keeps ownership of.  The
+ *            library allocates nothing and keeps no state between calls; it
+ *            is re-entrant and may be called concurrently on different
+ *            streams.  o and lse must not overlap q, k, v or each other.
+ *            Every pointer must be 16-byte aligned.
+ * Stream:    the work is enqueued on `stream` (NULL = the null stream) and
+ *            the call returns without waiting for it.
+ * LSE:       lse[b,h,i] = ln( sum_{j visible to i} exp(scale * q_i . k_j) ),
+ *            in fp32.  (The pages keep the row maximum m and sum l, first
+ *            page, section 4, last steps of Algorithm 1; this library returns
+ *            the single number m*scale + ln(l) instead.)
+ * Shapes:    B, H, N >= 1; N <= 2^30; d is 64 or 128; B*H*N*d < 2^40.
+ * scale:     finite and > 0 (usually 1/sqrt(d)).
+ * causal:    0 = no mask, any other value = top-left causal mask.
+ * Errors:    all argument checks run before anything is enqueued; a failed
+ *            check returns its code and touches no memory.  After a launch,
+ *            a HIP launch error is reported as FA_ERR_HIP.  Errors that
+ *            happen later on the device surface at the caller's next
+ *            synchronisation, as for any asynchronous HIP work.  No C++
+ *            exception crosses this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,     /* a required pointer is NULL                       */
+    FA_ERR_SHAPE = 2,    /* B, H or N < 1, N > 2^30, or B*H*N*d >= 2^40      */
+    FA_ERR_HEADDIM = 3,  /* d is not 64 or 128                               */
+    FA_ERR_SCALE = 4,    /* scale is not finite, or not > 0                  */
+    FA_ERR_ALIGN = 5,    /* a pointer is not 16-byte aligned                 */
+    FA_ERR_HIP = 6,      /* the kernel launch failed (hipGetLastError)       */
+    FA_ERR_ALIAS = 7     /* o or lse overlaps an input or each other         */
+};
+
+/*
+ * fa_fwd -- bf16 inputs and output, fp32 accumulation.
+ *   q, k, v : const bf16 [B, H, N, d]   (bf16 = IEEE binary32 upper half)
+ *   o       : bf16 [B, H, N, d], written; each element rounded to nearest
+ *             even from the fp32 result
+ *   lse     : fp32 [B, H, N], written
+ * Scores, softmax statistics and the output accumulator are fp32; the
+ * probabilities are rounded to bf16 before they multiply V (the row sums use
+ * the unrounded fp32 values).  Returns an fa_status code.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int N, int d, float scale, int causal,
+           hipStream_t stream);
+
+/*
+ * fa_fwd_f32 -- the same operation with fp32 inputs and output and fp32
+ * arithmetic throughout (no rounding to a narrower type anywhere).
+ * Same parameter list and conventions as fa_fwd.
+ */
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
+               float *lse, int B, int H, int N, int d, float scale, int causal,
+               hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,98 @@
+"""The C ABI of libfa on the CPU: the library loads, exports every function
+include/fa.h declares, and rejects bad arguments with the documented codes
+before anything reaches the GPU (every call here fails validation, so no HIP
+runtime call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_32_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == sorted(fa.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} missing from {fa.LIB_PATH}"
+
+
+def test_status_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"\b(FA_\w+)\s*=\s*(\d+)", text))
+    for name, value in codes.items():
+        assert getattr(fa, name) == value, name
+
+
+def test_strerror(lib):
+    for code in range(8):
+        s = fa.fa_strerror(code)
+        assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM",
+                             "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP",
+                             "FA_ERR_ALIAS"][code])
+    assert "unknown" in fa.fa_strerror(99)
+    assert "unknown" in fa.fa_strerror(-1)
+
+
+# Fake, well separated, 16-byte aligned addresses: validation rejects every
+# call below before any of them could be dereferenced.
+BASE = 1 << 40
+GAP = 1 << 36
+Q, K, V, O, L = (BASE + i * GAP for i in range(5))
+GOOD = dict(B=2, H=3, N=100, d=64, scale=0.125, causal=1)
+
+
+def _call(fn, q=Q, k=K, v=V, o=O, lse=L, **kw):
+    args = dict(GOOD)
+    args.update(kw)
+    return fn(q, k, v, o, lse, args["B"], args["H"], args["N"], args["d"],
+              args["scale"], args["causal"], None)
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_validation_codes(fn, lib):
+    assert _call(fn, q=0) == fa.FA_ERR_NULL
+    assert _call(fn, lse=0) == fa.FA_ERR_NULL
+    assert _call(fn, o=0, B=0) == fa.FA_ERR_NULL          # NULL is checked first
+    assert _call(fn, B=0) == fa.FA_ERR_SHAPE
+    assert _call(fn, H=-1) == fa.FA_ERR_SHAPE
+    assert _call(fn, N=0) == fa.FA_ERR_SHAPE
+    assert _call(fn, N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
+    assert _call(fn, B=1 << 16, H=1 << 10, N=1 << 10) == fa.FA_ERR_SHAPE  # 2^42 elements
+    for d in (0, 16, 32, 48, 96, 127, 256):
+        assert _call(fn, d=d) == fa.FA_ERR_HEADDIM
+    for s in (0.0, -0.125, float("inf"), float("nan")):
+        assert _call(fn, scale=s) == fa.FA_ERR_SCALE
+    assert _call(fn, q=Q + 8) == fa.FA_ERR_ALIGN
+    assert _call(fn, lse=L + 4) == fa.FA_ERR_ALIGN
+    assert _call(fn, o=Q) == fa.FA_ERR_ALIAS
+    assert _call(fn, o=K + 16) == fa.FA_ERR_ALIAS
+    assert _call(fn, lse=V + 1024) == fa.FA_ERR_ALIAS
+    esize = 2 if fn is fa.fa_fwd else 4
+    nbytes = 2 * 3 * 100 * 64 * esize
+    assert _call(fn, lse=O + nbytes - 16) == fa.FA_ERR_ALIAS
+    # adjacent but not overlapping is fine as far as aliasing goes; make the
+    # call fail on the shape instead so that nothing is launched
+    assert _call(fn, o=Q + nbytes, B=0) == fa.FA_ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from exact_attention_32_amd import _lib
+
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load_library(str(tmp_path / "missing.so"))

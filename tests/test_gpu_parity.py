@@ -1,0 +1,171 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Gates (fixed by the method's specification):
+  fp32 inputs : max |O_gpu - O_ref| <= 1e-5
+  bf16 inputs : max |O_gpu - O_ref| <= 2e-2 and
+                ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 5e-3 (over the whole tensor)
+  LSE         : max |LSE_gpu - LSE_ref| <= 1e-3 in every case
+Both sides read the same rounded inputs; the oracle widens them to fp64.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_32_amd as fa
+from exact_attention_32_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16_ABS = 2e-2
+TOL_BF16_REL = 5e-3
+TOL_LSE = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(q, k, v, causal, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def check(o, lse, o_ref, lse_ref, dtype, what):
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    err = np.abs(o - o_ref)
+    max_abs = float(err.max())
+    rel = float(np.linalg.norm((o - o_ref).ravel()) / np.linalg.norm(o_ref.ravel()))
+    lse_err = float(np.abs(lse - lse_ref).max())
+    _say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse={lse_err:.3e}")
+    if dtype == "f32":
+        assert max_abs <= TOL_F32, f"{what}: max abs {max_abs}"
+    else:
+        assert max_abs <= TOL_BF16_ABS, f"{what}: max abs {max_abs}"
+        assert rel <= TOL_BF16_REL, f"{what}: rel-L2 {rel}"
+    assert lse_err <= TOL_LSE, f"{what}: LSE {lse_err}"
+
+
+def full_case(w, oracle_lib):
+    _say(f"case {w.name} B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    q, k, v = inputs.make_qkv(w)
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    o_ref, lse_ref = oracle_lib.attention(q, k, v, w.scale, w.causal)
+    check(o, lse, o_ref, lse_ref, w.dtype, w.name)
+    return q, k, v, o, lse
+
+
+# --- the workloads at full size where the oracle finishes in seconds -------
+@pytest.mark.parametrize("name", ["w1_f32_n256_d64", "w2_bf16_b4h16_n2048_d64",
+                                  "w5a_bf16_b16h12_n1000_d64",
+                                  "w5b_bf16_b16h12_n1000_d64_causal"])
+def test_workload_full_tensor(name, oracle_lib):
+    full_case(inputs.WORKLOADS[name], oracle_lib)
+
+
+# --- the two largest workloads: sampled rows, computed one by one ----------
+@pytest.mark.parametrize("name", ["w3_bf16_b2h32_n8192_d128_causal",
+                                  "w4_bf16_b1h16_n16384_d64_causal_big_logits"])
+def test_workload_sampled_rows(name, oracle_lib):
+    w = inputs.WORKLOADS[name]
+    _say(f"case {w.name} (sampled rows)")
+    q, k, v = inputs.make_qkv(w)
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    rows = inputs.sample_rows(w, 384)
+    # every causal row 0 sees exactly key 0: O[0] must equal V[0] bit for bit
+    o0 = o[:, :, 0]
+    v0 = v[:, :, 0].float().double().numpy()
+    assert np.array_equal(o0, v0), "causal row 0 differs from V[0]"
+    o_ref, lse_ref = oracle_lib.attention_rows(q, k, v, w.scale, w.causal, rows)
+    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    got_lse = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    check(got, got_lse, o_ref, lse_ref, w.dtype, w.name + " sampled")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# --- reduced shapes: several tiles, ragged tails, both head dims -------------
+SMALL = [
+    # (B, H, N, d, dtype, dist, causal)
+    (1, 1, 1, 64, "bf16", "normal", False),
+    (1, 1, 1, 128, "bf16", "normal", True),
+    (1, 2, 63, 64, "bf16", "normal", True),
+    (1, 2, 64, 128, "bf16", "normal", False),
+    (2, 1, 65, 64, "bf16", "uniform", True),
+    (1, 3, 127, 128, "bf16", "normal", True),
+    (1, 3, 128, 64, "bf16", "normal4", True),
+    (2, 2, 129, 128, "bf16", "normal", False),
+    (1, 2, 300, 128, "bf16", "normal4", True),
+    (2, 3, 1000, 128, "bf16", "uniform", True),
+    (1, 2, 1000, 128, "bf16", "normal", False),
+    (1, 4, 2048, 128, "bf16", "normal", True),
+    (1, 2, 777, 64, "bf16", "normal4", False),
+    (1, 1, 1, 64, "f32", "normal", True),
+    (1, 2, 100, 64, "f32", "normal", True),
+    (2, 1, 300, 128, "f32", "normal", False),
+    (1, 2, 257, 128, "f32", "uniform", True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,dist,causal", SMALL)
+def test_small_shapes(B, H, N, d, dtype, dist, causal, oracle_lib):
+    w = inputs.Workload(f"small_{B}x{H}x{N}x{d}_{dtype}_{dist}_{int(causal)}",
+                        B, H, N, d, dtype, dist, causal, seed=1000 + N + d)
+    full_case(w, oracle_lib)
+
+
+def test_scale_values(oracle_lib):
+    """scale is applied in fp32 on the GPU; any positive value works."""
+    base = inputs.Workload("scale", 1, 2, 200, 64, "bf16", "normal", True, seed=77)
+    q, k, v = inputs.make_qkv(base)
+    for scale in (1.0, 0.01, 0.3):
+        o, lse = run_gpu(q, k, v, True, scale)
+        o_ref, lse_ref = oracle_lib.attention(q, k, v, float(np.float32(scale)), True)
+        check(o, lse, o_ref, lse_ref, "bf16", f"scale={scale}")
+
+
+def test_deterministic_and_stream_ordered():
+    """Two runs give bit-identical results, also on a side stream."""
+    w = inputs.WORKLOADS["w5b_bf16_b16h12_n1000_d64_causal"]
+    q, k, v = (t.cuda() for t in inputs.make_qkv(w))
+    o1, l1 = fa.forward(q, k, v, causal=True, scale=w.scale)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2, l2 = fa.forward(q, k, v, causal=True, scale=w.scale, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_result_independent_of_neighbours(oracle_lib):
+    """A head's result does not depend on what the other heads hold."""
+    w = inputs.Workload("nb", 2, 3, 333, 128, "bf16", "normal", True, seed=9)
+    q, k, v = inputs.make_qkv(w)
+    o, lse = run_gpu(q, k, v, True, w.scale)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in (q2, k2, v2):
+        t[0, 0] = 0
+        t[1, 2] = 7
+    o2, lse2 = run_gpu(q2, k2, v2, True, w.scale)
+    assert np.array_equal(o[0, 1:], o2[0, 1:]) and np.array_equal(o[1, :2], o2[1, :2])
+    assert np.array_equal(lse[0, 1:], lse2[0, 1:])
+
+
+def test_error_codes_on_device():
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    k, v = torch.zeros_like(q), torch.zeros_like(q)
+    with pytest.raises(fa.FAError) as e:
+        fa.forward(q, k, v, scale=-1.0)
+    assert e.value.code == fa.FA_ERR_SCALE
+    with pytest.raises(fa.FAError) as e:
+        fa.forward(q, k, v, out=q)
+    assert e.value.code == fa.FA_ERR_ALIAS
+    q3 = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.forward(q3, q3.clone(), q3.clone())
+    assert e.value.code == fa.FA_ERR_HEADDIM
