@@ -18,8 +18,11 @@ the fp64 oracle on a bounded sample of rows of the same workload.
 Counter helpers (used to produce the summaries under profiles/):
   python bench.py --copy-calibration ...   also runs one plain device copy
                                            of 1 GiB (for counter scaling)
-  python bench.py --summarize-counters DIR  turn rocprofv3 --pmc output
-                                           into the text summary
+  python bench.py --summarize-trace DIR CMD       per-kernel summary of a
+                                                  --kernel-trace --stats run
+  python bench.py --summarize-counters FDIR WDIR WORKLOAD CMD
+                                                  traffic summary of the
+                                                  FETCH_SIZE / WRITE_SIZE runs
 """
 from __future__ import annotations
 
@@ -103,31 +106,61 @@ def cpu_baseline(w, q, k, v, target_s: float):
     }
 
 
-def summarize_counters(directory: str) -> None:
-    """Print the traffic summary from two rocprofv3 --pmc runs (one with
-    FETCH_SIZE, one with WRITE_SIZE, both of `bench.py --copy-calibration`)
-    found under `directory`."""
-    import csv
+def _db_rows(directory: str, query: str):
+    import sqlite3
 
-    per_counter = {}
-    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
-                          recursive=True):
-        for row in csv.DictReader(open(path)):
-            name = row.get("Counter_Name") or row.get("Counter-Name")
-            kern = row.get("Kernel_Name") or row.get("Kernel-Name") or ""
-            val = float(row.get("Counter_Value") or row.get("Counter-Value"))
-            disp = row.get("Dispatch_Id") or row.get("Dispatch-Id")
-            per_counter.setdefault(name, {}).setdefault((kern, disp), 0.0)
-            per_counter[name][(kern, disp)] += val
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*_results.db"), recursive=True)):
+        con = sqlite3.connect(path)
+        rows += list(con.execute(query))
+        con.close()
+    return rows
+
+
+def summarize_trace(directory: str, command: str) -> None:
+    """Print the per-kernel summary of a `rocprofv3 --kernel-trace --stats`
+    run (SQLite output under `directory`)."""
+    print(f"COMMAND: {command}")
+    print("KERNEL_SOURCE_SHA256_16:", kernel_source_hash())
+    print("kernel | calls | total_ms | average_us | percent")
+    for name, calls, total, avg, pct in _db_rows(
+            directory, "select name, total_calls, total_duration, average, percentage "
+                       "from top_kernels"):
+        # rocprofv3 reports these two columns in microseconds
+        print(f"{name} | {calls} | {total / 1e3:.3f} | {avg:.2f} | {pct:.1f}")
+    for name, vgpr, agpr, sgpr, lds, scratch in _db_rows(
+            directory, "select distinct name, vgpr_count, accum_vgpr_count, sgpr_count, "
+                       "lds_size, scratch_size from kernels"):
+        print(f"resources {name}: vgpr={vgpr} agpr={agpr} sgpr={sgpr} lds={lds} scratch={scratch}")
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> None:
+    """Print the traffic summary of two `rocprofv3 --pmc` runs of
+    `bench.py --copy-calibration` (FETCH_SIZE in `fetch_dir`, WRITE_SIZE in
+    `write_dir`).  Each counter is scaled by COPY_BYTES / (its reading for
+    the plain device copy of COPY_BYTES that the same run performs)."""
+    q = "select kernel_name, value from counters_collection where counter_name = '%s'"
     out = {}
-    for name, d in per_counter.items():
-        fa_vals = [v for (kern, _), v in d.items() if "fwd_bf16_kernel" in kern]
-        cp_vals = [v for (kern, _), v in d.items()
-                   if "fwd_" not in kern and v * 1024 > COPY_BYTES / 4]
-        out[name] = (fa_vals, cp_vals)
-    for name, (fa_vals, cp_vals) in out.items():
-        print(f"{name}: fa launches={len(fa_vals)} mean={sum(fa_vals)/max(1,len(fa_vals)):.1f} KiB;"
-              f" copy kernels={len(cp_vals)} values={cp_vals}")
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _db_rows(d, q % counter)
+        fa_kib = [v for k, v in rows if "fwd_bf16_kernel" in k]
+        copy_kib = [v for k, v in rows if "copyBuffer" in k]
+        if not fa_kib or len(copy_kib) != 1:
+            raise SystemExit(f"{counter}: expected attention launches and one copy in {d}")
+        factor = COPY_BYTES / (copy_kib[0] * 1024.0)
+        mean = sum(fa_kib) / len(fa_kib)
+        out[counter] = (mean, factor, fa_kib, copy_kib[0])
+    print(f"COMMAND: {command}")
+    print(f"WORKLOAD: {workload}")
+    print(f"KERNEL_SOURCE_SHA256_16: {kernel_source_hash()}")
+    total = 0
+    for counter, (mean, factor, vals, copy) in out.items():
+        scaled = mean * 1024.0 * factor
+        total += scaled
+        print(f"{counter}_KIB_PER_LAUNCH: {mean:.1f} (launches: {', '.join(f'{v:.1f}' for v in vals)})")
+        print(f"{counter}_COPY_KIB: {copy:.1f} for a copy of {COPY_BYTES} bytes -> factor {factor:.4f}")
+        print(f"{counter}_BYTES_PER_LAUNCH_SCALED: {scaled:.0f}")
+    print(f"HBM_BYTES_PER_LAUNCH: {total:.0f}")
 
 
 def main() -> int:
@@ -139,11 +172,16 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
+    ap.add_argument("--summarize-counters", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "WORKLOAD", "COMMAND"))
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
+        summarize_counters(*args.summarize_counters)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
