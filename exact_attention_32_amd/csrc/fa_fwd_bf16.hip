@@ -58,38 +58,29 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = 4 * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                // keys per tile
 
-// Shared-memory tiles, unpadded; 16-byte chunks are XOR-swizzled by row so
-// that both the staging writes and the MFMA operand reads spread over the
-// LDS banks.
-//   K tile : [kBc keys][D], chunk c of row r lives at chunk c ^ (r & 7).
-//   Vt tile: [D][kBc keys, permuted], chunk c of row r at c ^ ((r ^ r>>3) & 7).
-template <int D>
-struct Tiles {
-    __bf16 k[2][kBc * D];
-    __bf16 vt[2][D * kBc];
-};
+// Shared-memory tiles.  Both are [kBc keys][D] row-major, unpadded; the
+// 16-byte chunks of a row are XOR-swizzled so that the MFMA operand reads hit
+// distinct banks:
+//   K tile: logical chunk c of row r is stored at chunk c ^ (r & 7)
+//           (the 8 rows read together by one 128-bit read spread over 8 banks);
+//   V tile: logical chunk c of row r is stored at chunk c ^ (2 * (r & 3))
+//           (the 4 rows x 2 chunks of one 16-lane transpose read spread over
+//           8 banks).
+// Tiles are filled by buffer loads that write LDS directly: lane l of a load
+// instruction lands at LDS byte 16*l after the instruction's base, so the
+// swizzle is applied on the global (gather) side.  Rows beyond N are outside
+// the buffer's range and arrive as zeros.
+__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
 
-template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk) {
-    return row * D + ((chunk ^ (row & 7)) << 3);
-}
-
-__device__ __forceinline__ int vt_off(int row, int chunk) {
-    return row * kBc + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
-}
-
-// Position of key x (0..kBc-1) inside a transposed V row: bits 2 and 3 of the
-// key index are swapped, so that the 8 keys one lane feeds to the PV MFMA
-// (keys 16t + 4g + {0..3} and 16t + 8 + 4g + {0..3}) are contiguous.
-__device__ __forceinline__ int key_perm(int x) {
-    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
+#define LDS3 __attribute__((address_space(3)))
 
 // Workgroup id -> (batch*head, query tile).  Consecutive ids go to
 // consecutive XCDs; when the grid divides evenly, XCD x receives the
@@ -110,19 +101,55 @@ __device__ __forceinline__ u32x4 load16(const __bf16 *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Buffer descriptor over `bytes` bytes starting at `base` (raw, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Enqueue the direct-to-LDS loads of one K tile and one V tile (keys c0 ..
+// c0 + kBc - 1) into dk / dv.  Each call issues kLoads 16-byte loads per lane
+// for each operand; rows at or beyond N read as zeros.  (Kept out of the
+// kernel's lambdas: a buffer descriptor local in a lambda makes the host
+// pass drop the kernel's launch stub.)
+template <int D, int kLoads>
+__device__ __forceinline__ void issue_tile_loads(const __bf16 *Kh, const __bf16 *Vh, int N,
+                                                 int c0, LDS3 char *dk, LDS3 char *dv,
+                                                 const uint32_t *k_src, const uint32_t *v_src,
+                                                 int wave) {
+    const uint32_t bytes = (uint32_t)min(kBc, N - c0) * (uint32_t)(D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int pos = (u * 4 + wave) * 64 * 16;  // byte offset of this wave's 1 KiB
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
+    }
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 const __bf16 *__restrict__ V, __bf16 *__restrict__ O,
                 float *__restrict__ LSE, int N, int nqt, float scale, float scale_log2) {
     static_assert(D == 64 || D == 128, "head dim");
-    __shared__ __attribute__((aligned(16))) Tiles<D> sm;
+    constexpr int kChunksPerRow = D / 8;                        // 16-byte chunks
+    constexpr int kLoads = kBc * kChunksPerRow / kThreads;     // per thread per tile
+    // Two buffers per operand as four distinct objects: the tile loop is
+    // unrolled by two so that every access names its buffer at compile time,
+    // which lets the compiler see that the loads filling one buffer do not
+    // touch the one being read (no wait on the in-flight loads).
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k0[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k1[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v0[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v1[kBc * D];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int g = lane >> 5;  // half-wave
-    const int j = lane & 31;  // query column of this lane
+    const int j = lane & 31;  // query column of this lane (S^T / O^T layouts)
 
     int bh, qt;
     map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
@@ -146,6 +173,47 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int kv_end = CAUSAL ? min(N, r0 + kBr) : N;
     const int n_tiles = (kv_end + kBc - 1) / kBc;
 
+    // ---- staging offsets (lane constants) ---------------------------------
+    // Load u of wave w fills LDS chunk positions [(u*4 + w)*64, +64); lane l
+    // fills position q = that base + l, i.e. row q / kChunksPerRow, stored
+    // chunk q % kChunksPerRow, and must fetch the logical chunk that the
+    // swizzle puts there.
+    uint32_t k_src[kLoads], v_src[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int q = (u * 4 + wave) * 64 + lane;
+        const int r = q / kChunksPerRow;
+        const int p = q % kChunksPerRow;
+        k_src[u] = (uint32_t)(r * D * 2 + ((p ^ k_swz(r)) << 4));
+        v_src[u] = (uint32_t)(r * D * 2 + ((p ^ v_swz(r)) << 4));
+    }
+    auto issue_tile = [&](int c0, LDS3 char *dk, LDS3 char *dv) {
+        issue_tile_loads<D, kLoads>(Kh, Vh, N, c0, dk, dv, k_src, v_src, wave);
+    };
+
+    // MFMA operand read offsets (bytes within a tile).
+    // K (A operand of S^T = K Q^T): lane (g, j) reads row 32kb + j, logical
+    // chunk 2ks + g.
+    uint32_t k_rd[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        k_rd[ks] = (uint32_t)(j * D * 2 + (((2 * ks + g) ^ k_swz(j)) << 4));
+    // V^T (A operand of O^T += V^T P^T) through the 16-lane transpose read:
+    // in group G = lane/16 (m0 = 16*(G&1), g = G>>1), lane i of the group reads
+    // row 16T + 8h + 4g + i/4, columns 32db + m0 + 4(i%4) .. +3.  The row's
+    // low two bits are i/4, so the swizzle term is a lane constant; only the
+    // parity of db changes the stored chunk.
+    const int gi = lane & 15;
+    const int m0 = 16 * ((lane >> 4) & 1);
+    uint32_t v_rd[2];
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+        const int row = 4 * g + (gi >> 2);
+        const int col = 32 * odd + m0 + 4 * (gi & 3);
+        const int c = col >> 3;
+        v_rd[odd] = (uint32_t)(row * D * 2 + ((c ^ v_swz(row)) << 4) + ((col & 4) << 1));
+    }
+
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -154,108 +222,47 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     float m_run = -INFINITY;  // running max of the raw scores of row qrow
     float l_run = 0.f;        // this half-wave's share of the running sum
 
-    // ---- staging: global -> registers -> LDS ------------------------------
-    constexpr int kKChunks = kBc * D / 8 / kThreads;  // 16-byte K chunks per thread
-    constexpr int kVUnits = (kBc / 4) * (D / 8);      // 4-key x 8-column V blocks
-    u32x4 kreg[kKChunks];
-    u32x4 vreg[4];
+    LDS3 char *const k0 = (LDS3 char *)lds_k0;
+    LDS3 char *const k1 = (LDS3 char *)lds_k1;
+    LDS3 char *const v0 = (LDS3 char *)lds_v0;
+    LDS3 char *const v1 = (LDS3 char *)lds_v1;
 
-    auto load_tile = [&](int c0) {
-#pragma unroll
-        for (int u = 0; u < kKChunks; ++u) {
-            const int chunk = tid + kThreads * u;
-            const int row = chunk / (D / 8);
-            const int c = chunk % (D / 8);
-            const int key = c0 + row;
-            kreg[u] = u32x4{0u, 0u, 0u, 0u};
-            if (key < N) kreg[u] = load16(Kh + (size_t)key * D + c * 8);
-        }
-        if (tid < kVUnits) {
-            const int c = tid % (D / 8);
-            const int kq = tid / (D / 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = c0 + 4 * kq + e;
-                vreg[e] = u32x4{0u, 0u, 0u, 0u};
-                if (key < N) vreg[e] = load16(Vh + (size_t)key * D + c * 8);
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < kKChunks; ++u) {
-            const int chunk = tid + kThreads * u;
-            const int row = chunk / (D / 8);
-            const int c = chunk % (D / 8);
-            *reinterpret_cast<u32x4 *>(&sm.k[buf][k_off<D>(row, c)]) = kreg[u];
-        }
-        if (tid < kVUnits) {
-            // vreg[e] = V[4kq+e][8c .. 8c+7]; dword h holds columns 8c+2h (low
-            // half) and 8c+2h+1 (high half).  Write column 8c+2h (+1) of the
-            // four keys as one 8-byte row segment of the transposed tile.
-            const int c = tid % (D / 8);
-            const int kq = tid / (D / 8);
-            const int col = key_perm(4 * kq);
-            const int chunk = col >> 3;
-            const int half = (col >> 2) & 1;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const uint32_t a0 = vreg[0][h], a1 = vreg[1][h];
-                const uint32_t a2 = vreg[2][h], a3 = vreg[3][h];
-                u32x2 lo, hi;
-                lo[0] = (a0 & 0xffffu) | (a1 << 16);
-                lo[1] = (a2 & 0xffffu) | (a3 << 16);
-                hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-                const int row = 8 * c + 2 * h;
-                *reinterpret_cast<u32x2 *>(&sm.vt[buf][vt_off(row, chunk) + 4 * half]) = lo;
-                *reinterpret_cast<u32x2 *>(&sm.vt[buf][vt_off(row + 1, chunk) + 4 * half]) = hi;
-            }
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
+    // One key tile: prefetch the next tile into the other buffers, then
+    // S^T, softmax and O^T on this one.
+    auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk,
+                    LDS3 char *nv) {
         const int c0 = t * kBc;
-        const bool has_next = t + 1 < n_tiles;
-        if (has_next) load_tile(c0 + kBc);
+        if (t + 1 < n_tiles) issue_tile(c0 + kBc, nk, nv);
 
         // A wave whose rows all precede this tile has nothing to add.
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
         if (active) {
-            const __bf16 *kt = sm.k[buf];
-            const __bf16 *vt = sm.vt[buf];
 
             // S^T[key][query] = K Q^T for the kBc keys of this tile.
             f32x16 s[kBc / 32];
 #pragma unroll
-            for (int kb = 0; kb < kBc / 32; ++kb) {
+            for (int kb = 0; kb < kBc / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        kt + k_off<D>(32 * kb + j, 2 * ks + g));
+            for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < kBc / 32; ++kb) {
+                    const bf16x8 a = *reinterpret_cast<const LDS3 bf16x8 *>(
+                        kt + k_rd[ks] + kb * 32 * D * 2);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s[kb], 0, 0, 0);
                 }
-            }
 
             // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
             const bool need_mask = (CAUSAL && c0 + kBc - 1 > wrow0) || (c0 + kBc > N);
             if (need_mask) {
+                // visible iff 32kb + 8(r/4) + r%4 <= lim, lim = min(qrow, N-1) - c0 - 4g
+                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - c0 - 4 * g;
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = c0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                        const bool hidden = key >= N || (CAUSAL && key > qrow);
-                        if (hidden) s[kb][r] = -INFINITY;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
             }
 
             // Tile row maximum: in-register, then across the two half-waves.
@@ -264,7 +271,11 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int kb = 0; kb < kBc / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                                 __float_as_uint(mt), false, false);
+                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
             const float m_new = fmaxf(m_run, mt);
             // A row that has seen no visible key keeps base 0 (its terms are 0).
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -298,23 +309,44 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             }
             m_run = m_new;
 
-            // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15.
+            // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15, the
+            // A operand is two transpose reads (keys 16T+4g+k, 16T+8+4g+k).
 #pragma unroll
             for (int T = 0; T < kBc / 16; ++T)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        vt + vt_off(32 * db + j, 2 * T + g));
+                    const LDS3 char *base = vt + v_rd[db & 1] + (db >> 1) * 128 + T * 16 * D * 2;
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS3 v4i16 *)(base));
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS3 v4i16 *)(base + 8 * D * 2));
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[T], acc[db], 0, 0, 0);
                 }
         }
 
-        if (has_next) store_tile(buf ^ 1);
+        // The next tile's loads must have landed before anyone reads them, and
+        // every wave must be done with this tile before it is overwritten.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    issue_tile(0, k0, v0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, k0, v0, k1, v1);
+        if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
     }
 
     // Epilogue: O = acc / l, rounded to bf16; LSE = m*scale + ln(l).
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                         __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     const float inv = 1.f / l_tot;
     if (qrow < N) {
         __bf16 *orow = O + hoff + (size_t)qrow * D;
