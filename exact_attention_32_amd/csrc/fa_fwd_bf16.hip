@@ -67,18 +67,30 @@ constexpr int kBc = 64;                // keys per tile
 
 // Shared-memory tiles.  Both are [kBc keys][D] row-major, unpadded; the
 // 16-byte chunks of a row are XOR-swizzled so that the MFMA operand reads hit
-// distinct banks:
-//   K tile: logical chunk c of row r is stored at chunk c ^ (r & 7)
-//           (the 8 rows read together by one 128-bit read spread over 8 banks);
-//   V tile: logical chunk c of row r is stored at chunk c ^ (2 * (r & 3))
-//           (the 4 rows x 2 chunks of one 16-lane transpose read spread over
-//           8 banks).
+// distinct banks.  gfx950's LDS serves these reads 256 bytes at a time (16
+// lanes of a 128-bit read, 32 lanes of a 64-bit read), so each group of
+// chunks read together must land on 16 distinct 16-byte bank groups
+// (measured with SQ_LDS_BANK_CONFLICT on candidate layouts):
+//   K tile, read 16 rows x one chunk at a time:
+//     d = 128: chunk c of row r stored at c ^ (r & 15);
+//     d = 64 : two rows share a 256-byte line, chunk stored at c ^ ((r >> 1) & 7);
+//   (both depend on r mod 32 only, so the reads of the second 32-row block
+//   reuse the first block's offsets plus a constant);
+//   V tile, read 4 rows x 4 chunks at a time by the transpose read:
+//     d = 128: chunk stored at c ^ (4 * (r & 3));
+//     d = 64 : chunk stored at c ^ (2 * (r & 3)).
 // Tiles are filled by buffer loads that write LDS directly: lane l of a load
 // instruction lands at LDS byte 16*l after the instruction's base, so the
 // swizzle is applied on the global (gather) side.  Rows beyond N are outside
 // the buffer's range and arrive as zeros.
-__device__ __forceinline__ int k_swz(int r) { return r & 7; }
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+    return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+}
 
 #define LDS3 __attribute__((address_space(3)))
 
@@ -184,8 +196,8 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         const int q = (u * 4 + wave) * 64 + lane;
         const int r = q / kChunksPerRow;
         const int p = q % kChunksPerRow;
-        k_src[u] = (uint32_t)(r * D * 2 + ((p ^ k_swz(r)) << 4));
-        v_src[u] = (uint32_t)(r * D * 2 + ((p ^ v_swz(r)) << 4));
+        k_src[u] = (uint32_t)(r * D * 2 + ((p ^ k_swz<D>(r)) << 4));
+        v_src[u] = (uint32_t)(r * D * 2 + ((p ^ v_swz<D>(r)) << 4));
     }
     auto issue_tile = [&](int c0, LDS3 char *dk, LDS3 char *dv) {
         issue_tile_loads<D, kLoads>(Kh, Vh, N, c0, dk, dv, k_src, v_src, wave);
@@ -197,21 +209,21 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     uint32_t k_rd[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-        k_rd[ks] = (uint32_t)(j * D * 2 + (((2 * ks + g) ^ k_swz(j)) << 4));
+        k_rd[ks] = (uint32_t)(j * D * 2 + (((2 * ks + g) ^ k_swz<D>(j)) << 4));
     // V^T (A operand of O^T += V^T P^T) through the 16-lane transpose read:
     // in group G = lane/16 (m0 = 16*(G&1), g = G>>1), lane i of the group reads
     // row 16T + 8h + 4g + i/4, columns 32db + m0 + 4(i%4) .. +3.  The row's
-    // low two bits are i/4, so the swizzle term is a lane constant; only the
-    // parity of db changes the stored chunk.
+    // low two bits are i/4, so the swizzle term is a lane constant and the
+    // offset depends on db only through the stored chunk.
     const int gi = lane & 15;
     const int m0 = 16 * ((lane >> 4) & 1);
-    uint32_t v_rd[2];
+    uint32_t v_rd[D / 32];
 #pragma unroll
-    for (int odd = 0; odd < 2; ++odd) {
+    for (int db = 0; db < D / 32; ++db) {
         const int row = 4 * g + (gi >> 2);
-        const int col = 32 * odd + m0 + 4 * (gi & 3);
+        const int col = 32 * db + m0 + 4 * (gi & 3);
         const int c = col >> 3;
-        v_rd[odd] = (uint32_t)(row * D * 2 + ((c ^ v_swz(row)) << 4) + ((col & 4) << 1));
+        v_rd[db] = (uint32_t)(row * D * 2 + ((c ^ v_swz<D>(row)) << 4) + ((col & 4) << 1));
     }
 
     f32x16 acc[D / 32];
@@ -315,7 +327,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int T = 0; T < kBc / 16; ++T)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const LDS3 char *base = vt + v_rd[db & 1] + (db >> 1) * 128 + T * 16 * D * 2;
+                    const LDS3 char *base = vt + v_rd[db] + T * 16 * D * 2;
                     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (LDS3 v4i16 *)(base));
                     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
