@@ -64,6 +64,9 @@ constexpr int kThreads = 256;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = 4 * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                // keys per tile
+// Growth of a row's maximum (in log2 units of the scaled logits) tolerated
+// before the exponent base and the accumulator are rescaled.
+constexpr float kRescaleLog2 = 8.f;
 
 // Shared-memory tiles.  Both are [kBc keys][D] row-major, unpadded; the
 // 16-byte chunks of a row are XOR-swizzled so that the MFMA operand reads hit
@@ -288,11 +291,20 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                                                                  __float_as_uint(mt), false, false);
                 mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
-            const float m_new = fmaxf(m_run, mt);
+            // Lazy rescale: the exponent base m_run moves to the new maximum only
+            // when the tile's maximum exceeds it by more than kRescaleLog2 (in
+            // log2 units of the scaled logits); otherwise the base is kept and
+            // the tile's probabilities are at most 2^kRescaleLog2 instead of 1.
+            // Numerator and denominator share the base, so O = acc / l and
+            // LSE = m_run*scale + ln(l) are unchanged, while the rescale of the
+            // accumulator (and its wave-wide branch) becomes rare.
+            const bool bump = m_run == -INFINITY ? mt != -INFINITY
+                                                 : (mt - m_run) * scale_log2 > kRescaleLog2;
+            const float m_new = bump ? mt : m_run;
             // A row that has seen no visible key keeps base 0 (its terms are 0).
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            // alpha from the OLD maximum, before it is replaced.
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+            // alpha from the OLD base, before it is replaced (exactly 1 if kept).
+            const float alpha = bump ? __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2) : 1.f;
             const float mc = m_use * scale_log2;
 
             // P = exp(scale*(s - m)) = 2^(s*scale*log2e - m*scale*log2e).
