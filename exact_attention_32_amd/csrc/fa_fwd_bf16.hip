@@ -259,13 +259,37 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int kb = 0; kb < kBc / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            // All K fragments of the tile are requested before the first MFMA,
+            // so the LDS latency is paid once per tile, not once per k-step.
+            bf16x8 kf[D / 16][kBc / 32];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-                for (int kb = 0; kb < kBc / 32; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const LDS3 bf16x8 *>(
+                for (int kb = 0; kb < kBc / 32; ++kb)
+                    kf[ks][kb] = *reinterpret_cast<const LDS3 bf16x8 *>(
                         kt + k_rd[ks] + kb * 32 * D * 2);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s[kb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < kBc / 32; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qop[ks], s[kb], 0,
+                                                                    0, 0);
+
+            // All V^T fragments of the tile are requested now; the softmax below
+            // covers their latency.  Fragment (T, db) is two transpose reads
+            // (keys 16T+4g+k and 16T+8+4g+k, columns of d-block db).
+            bf16x8 vf[kBc / 16][D / 32];
+#pragma unroll
+            for (int T = 0; T < kBc / 16; ++T)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const LDS3 char *base = vt + v_rd[db] + T * 16 * D * 2;
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base));
+                    const v4i16 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
+                    vf[T][db] = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
 
             // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
@@ -333,21 +357,13 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             }
             m_run = m_new;
 
-            // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15, the
-            // A operand is two transpose reads (keys 16T+4g+k, 16T+8+4g+k).
+            // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15.
 #pragma unroll
             for (int T = 0; T < kBc / 16; ++T)
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const LDS3 char *base = vt + v_rd[db] + T * 16 * D * 2;
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS3 v4i16 *)(base));
-                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS3 v4i16 *)(base + 8 * D * 2));
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[T], acc[db], 0, 0, 0);
-                }
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[T][db], pop[T], acc[db], 0,
+                                                                      0, 0);
         }
 
         // The next tile's loads must have landed before anyone reads them, and

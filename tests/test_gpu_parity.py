@@ -169,3 +169,27 @@ def test_error_codes_on_device():
     with pytest.raises(fa.FAError) as e:
         fa.forward(q3, q3.clone(), q3.clone())
     assert e.value.code == fa.FA_ERR_HEADDIM
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("order", ["growing", "shrinking"])
+def test_row_max_moves_across_tiles(order, causal, oracle_lib):
+    """Logits whose row maximum grows (or shrinks) by more than 2^8 from one
+    64-key tile to the next, so the exponent base of the online softmax is
+    moved and the accumulator rescaled at nearly every tile (and, in the
+    shrinking order, only at the first)."""
+    B, H, N, d = 1, 2, 700, 128
+    g = torch.Generator().manual_seed(41)
+    u = torch.randint(0, 2, (d,), generator=g).float() * 2 - 1          # +-1 direction
+    ramp = torch.linspace(0.0, 6.0, N) if order == "growing" else torch.linspace(6.0, 0.0, N)
+    q = 2.0 * u + 0.3 * torch.randn(B, H, N, d, generator=g)
+    k = ramp[None, None, :, None] * u + 0.3 * torch.randn(B, H, N, d, generator=g)
+    v = torch.randn(B, H, N, d, generator=g)
+    q, k, v = (t.to(torch.bfloat16).contiguous() for t in (q, k, v))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle_lib.attention(q, k, v, scale, causal)
+    # logit growth per 64-key tile, in log2 units: must exceed the 2^8 slack
+    per_tile = 2.0 * d * scale * (6.0 / N) * 64 / math.log(2)
+    assert per_tile > 8, per_tile
+    check(o, lse, o_ref, lse_ref, "bf16", f"row max {order} causal={causal}")
