@@ -15,27 +15,38 @@
 // ------------------
 // * One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
 //   wave owns 32 rows for the whole key loop (Q, the output accumulator and
-//   the running max / sum never leave registers).
-// * Key/value tiles of 64 keys are staged global -> registers -> LDS with
-//   16-byte loads, double-buffered: the loads of tile t+1 are issued before
-//   the matrix work of tile t and written to the other LDS buffer after it.
-// * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: with K as the A operand and Q^T
-//   as the B operand, lane (g, j) of the accumulator holds query j and 16 of
-//   the 32 keys of a block, so a row's max and sum are in-register reductions
-//   plus one exchange between the two half-waves.
+//   the running max / sum never leave registers).  Two workgroups share a
+//   compute unit, i.e. each SIMD runs one wave of each.
+// * Key/value tiles of 64 keys are copied global -> LDS by buffer loads that
+//   write LDS directly (no registers; rows past N arrive as zeros), double
+//   buffered.  The loads of tile t+1 are spread over the S MFMAs of tile t
+//   and waited for at the end of tile t, before the workgroup barrier.
+// * LDS layout: both tiles row-major [key][d], 16-byte chunks XOR-swizzled
+//   per row so that the operand reads below are free of bank conflicts (the
+//   loads gather global chunks so that they land swizzled).
+// * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: with K as the A operand (one
+//   128-bit LDS read per fragment) and Q^T as the B operand, lane (g, j) of
+//   the accumulator holds query j and 16 of the 32 keys of a block, so a
+//   row's max and sum are in-register reductions plus one exchange between
+//   the two half-waves (v_permlane32_swap).
 // * O^T += V^T P^T on the same instruction: the probabilities leave the S
 //   accumulator already in the B-operand layout of this product (the 16
 //   accumulator rows of a lane are taken as the K index of the next MFMA),
-//   so P never goes through LDS.  V is transposed while it is staged into
-//   LDS, with the key order inside each 16-key group permuted to match.
+//   so P never goes through LDS; the V^T operand comes straight out of the
+//   row-major V tile through the LDS transpose read (ds_read_b64_tr_b16).
+// * All K fragments of a tile are requested before its first MFMA and all
+//   V^T fragments right after the last S MFMA, so each wave pays the LDS
+//   latency once per operand and tile.
 // * Causal: key tiles wholly in the future of the workgroup are never loaded
 //   (loop bound), a wave whose 32 rows are all before a tile skips its math,
 //   and only tiles that straddle the diagonal (or the ragged end of N) pay
 //   for the element-wise mask (unit-12 causal-mask lesson: skip / diagonal /
 //   past tiles).
-// * The running maximum is kept per row; the accumulator is rescaled by
-//   alpha = e^(m_old - m_new) only when some row's maximum moved (the factor
-//   is exactly 1 otherwise).
+// * Lazy rescale: a row's exponent base moves to its running maximum only
+//   when that maximum has grown by more than 2^8 (in base-2 units of the
+//   scaled logits) since the base was set; the accumulator is rescaled
+//   (wave-uniform branch) only then.  Numerator and denominator share the
+//   base, so O and the LSE are the same as with the exact running maximum.
 // * Grid: workgroups are dealt round-robin over the 8 XCDs; consecutive
 //   workgroup ids are remapped so that each XCD walks a contiguous range of
 //   heads (its 4 MB L2 then serves the K/V stream of one head to all its
@@ -60,9 +71,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kBr = 4 * kRowsPerWave;  // query rows per workgroup
+constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                // keys per tile
 // Growth of a row's maximum (in log2 units of the scaled logits) tolerated
 // before the exponent base and the accumulator are rescaled.
@@ -122,23 +134,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
-// Enqueue the direct-to-LDS loads of one K tile and one V tile (keys c0 ..
-// c0 + kBc - 1) into dk / dv.  Each call issues kLoads 16-byte loads per lane
-// for each operand; rows at or beyond N read as zeros.  (Kept out of the
-// kernel's lambdas: a buffer descriptor local in a lambda makes the host
-// pass drop the kernel's launch stub.)
+// Enqueue load number i (0 <= i < 2 kLoads) of the next key tile (keys c0 ..
+// c0 + kBc - 1): even i load K into dk, odd i load V into dv, load u = i/2
+// of this wave's share, one 16-byte direct-to-LDS load per lane.  Rows at or
+// beyond N read as zeros.  The loads of a tile are issued one at a time
+// between the MFMAs of the tile being computed: issued as one burst by every
+// wave, they fill the texture-address queue and the in-order wave stalls
+// behind them before it can start its MFMAs.  (Kept out of the kernel's
+// lambdas: a buffer descriptor local in a lambda makes the host pass drop the
+// kernel's launch stub.)
 template <int D, int kLoads>
-__device__ __forceinline__ void issue_tile_loads(const __bf16 *Kh, const __bf16 *Vh, int N,
-                                                 int c0, LDS3 char *dk, LDS3 char *dv,
-                                                 const uint32_t *k_src, const uint32_t *v_src,
-                                                 int wave) {
+__device__ __forceinline__ void issue_tile_load(int i, const __bf16 *Kh, const __bf16 *Vh, int N,
+                                                int c0, LDS3 char *dk, LDS3 char *dv,
+                                                const uint32_t *k_src, const uint32_t *v_src,
+                                                int wave) {
     const uint32_t bytes = (uint32_t)min(kBc, N - c0) * (uint32_t)(D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-        const int pos = (u * 4 + wave) * 64 * 16;  // byte offset of this wave's 1 KiB
+    const int u = i >> 1;
+    const int pos = (u * kWaves + wave) * 64 * 16;  // byte offset of this wave's 1 KiB
+    if ((i & 1) == 0) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
     }
 }
@@ -189,22 +206,22 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int n_tiles = (kv_end + kBc - 1) / kBc;
 
     // ---- staging offsets (lane constants) ---------------------------------
-    // Load u of wave w fills LDS chunk positions [(u*4 + w)*64, +64); lane l
+    // Load u of wave w fills LDS chunk positions [(u*kWaves + w)*64, +64); lane l
     // fills position q = that base + l, i.e. row q / kChunksPerRow, stored
     // chunk q % kChunksPerRow, and must fetch the logical chunk that the
     // swizzle puts there.
     uint32_t k_src[kLoads], v_src[kLoads];
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
-        const int q = (u * 4 + wave) * 64 + lane;
+        const int q = (u * kWaves + wave) * 64 + lane;
         const int r = q / kChunksPerRow;
         const int p = q % kChunksPerRow;
         k_src[u] = (uint32_t)(r * D * 2 + ((p ^ k_swz<D>(r)) << 4));
         v_src[u] = (uint32_t)(r * D * 2 + ((p ^ v_swz<D>(r)) << 4));
     }
-    auto issue_tile = [&](int c0, LDS3 char *dk, LDS3 char *dv) {
-        issue_tile_loads<D, kLoads>(Kh, Vh, N, c0, dk, dv, k_src, v_src, wave);
-    };
+    // The 2 kLoads tile loads are spread evenly over the D/16 k-steps of S.
+    constexpr int kLoadStride = (D / 16) / (2 * kLoads);
+    static_assert(kLoadStride >= 1 && kLoadStride * 2 * kLoads == D / 16, "load spacing");
 
     // MFMA operand read offsets (bytes within a tile).
     // K (A operand of S^T = K Q^T): lane (g, j) reads row 32kb + j, logical
@@ -247,10 +264,17 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk,
                     LDS3 char *nv) {
         const int c0 = t * kBc;
-        if (t + 1 < n_tiles) issue_tile(c0 + kBc, nk, nv);
+        const bool prefetch = t + 1 < n_tiles;
+        auto load = [&](int i) __attribute__((always_inline)) {
+            issue_tile_load<D, kLoads>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src, wave);
+        };
 
         // A wave whose rows all precede this tile has nothing to add.
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
+        if (!active && prefetch) {
+#pragma unroll
+            for (int i = 0; i < 2 * kLoads; ++i) load(i);
+        }
         if (active) {
 
             // S^T[key][query] = K Q^T for the kBc keys of this tile.
@@ -269,12 +293,23 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     kf[ks][kb] = *reinterpret_cast<const LDS3 bf16x8 *>(
                         kt + k_rd[ks] + kb * 32 * D * 2);
             __builtin_amdgcn_sched_barrier(0);
+            // The S MFMAs run at raised wave priority: the other wave on this
+            // SIMD (from another workgroup) then tends to run its softmax while
+            // this one keeps the matrix core busy, instead of both waves
+            // alternating instruction by instruction through the same phase.
+            __builtin_amdgcn_s_setprio(1);
+            // The next tile's loads go out one per k-step, between the MFMAs.
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
+            for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qop[ks], s[kb], 0,
                                                                     0, 0);
+                if (prefetch && ks % kLoadStride == 0) load(ks / kLoadStride);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            __builtin_amdgcn_s_setprio(0);
 
             // All V^T fragments of the tile are requested now; the softmax below
             // covers their latency.  Fragment (T, db) is two transpose reads
@@ -372,7 +407,9 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         __syncthreads();
     };
 
-    issue_tile(0, k0, v0);
+#pragma unroll
+    for (int i = 0; i < 2 * kLoads; ++i)
+        issue_tile_load<D, kLoads>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < n_tiles; t += 2) {
