@@ -1,7 +1,7 @@
 /*
  * oracle.c -- plain, slow, fp64 CPU reference for the exact attention forward
- * pass O = softmax(scale * Q K^T [+ causal mask]) V and its per-row
- * log-sum-exp.
+ * pass O = softmax(scale * Q K^T [+ causal mask]) V, its per-row log-sum-exp,
+ * and the gradients dQ, dK, dV of that forward pass (end of the file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the test suite, the smoke check and the benchmark's
@@ -164,6 +164,150 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
             score_row(qh + i * d, kh, i, N, d, scale, causal, s);
             lse_rows[r] = oracle_softmax(s, N, p);
             weighted_sum(p, vh, N, d, o_rows + r * d);
+        }
+        free(s);
+        free(p);
+    }
+    return failed ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward pass.  The pages say only that the backward pass recomputes S and P
+ * from Q, K and the statistics the forward pass keeps, instead of storing the
+ * N x N matrices ("解析 FlashAttention（2）", section 1.2 item (3) and the
+ * remark after Algorithm 1 that m and l are kept for the backward pass;
+ * Triton page section 5.1: dQ, dK and dV are all needed).  They give no
+ * formulas, so this is the derivative of the forward definition above by the
+ * chain rule, for a loss whose gradient with respect to O is dO:
+ *   dV = P^T dO                        (O = P V)
+ *   dP = dO V^T
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)   (Jacobian of each softmax row)
+ *   dQ = scale * dS K,  dK = scale * dS^T Q   (S = scale * Q K^T)
+ * Masked entries have P_ij = 0 exactly and so contribute nothing.  Sums run
+ * left to right in index order.
+ * ------------------------------------------------------------------------- */
+
+/* dP row i and its softmax-Jacobian product: given the probability row p and
+ * dO row i, writes ds[j] = p_j (dp_j - sum_k p_k dp_k), dp_j = dO_i . v_j. */
+static void grad_score_row(const double *p, const double *do_row, const double *v_head,
+                           long N, long d, double *ds)
+{
+    double dsum = 0.0;
+    for (long j = 0; j < N; ++j) {
+        double dp = 0.0;
+        if (p[j] != 0.0) {
+            const double *v_row = v_head + j * d;
+            for (long t = 0; t < d; ++t)
+                dp += do_row[t] * v_row[t];
+        }
+        ds[j] = dp; /* dP, turned into dS below */
+        dsum += p[j] * dp;
+    }
+    for (long j = 0; j < N; ++j)
+        ds[j] = p[j] * (ds[j] - dsum);
+}
+
+/* Full backward pass with S, P and dS materialised per (b, h).  dout is
+ * [B, H, N, d]; dq, dk, dv receive [B, H, N, d].  Returns 0, or -1 when memory
+ * for the N x N matrices runs out. */
+int oracle_attention_backward(const double *q, const double *k, const double *v,
+                              const double *dout, long B, long H, long N, long d,
+                              double scale, int causal, double *dq, double *dk,
+                              double *dv)
+{
+    double *P = (double *)malloc((size_t)N * (size_t)N * sizeof(double));
+    double *dS = (double *)malloc((size_t)N * (size_t)N * sizeof(double));
+    if (!P || !dS) {
+        free(P);
+        free(dS);
+        return -1;
+    }
+    for (long bh = 0; bh < B * H; ++bh) {
+        const double *qh = q + bh * N * d;
+        const double *kh = k + bh * N * d;
+        const double *vh = v + bh * N * d;
+        const double *doh = dout + bh * N * d;
+        double *dqh = dq + bh * N * d;
+        double *dkh = dk + bh * N * d;
+        double *dvh = dv + bh * N * d;
+        /* P = softmax(scale * Q K^T + mask), row by row (dS holds S meanwhile) */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            score_row(qh + i * d, kh, i, N, d, scale, causal, dS + i * N);
+            oracle_softmax(dS + i * N, N, P + i * N);
+        }
+        /* dS = P o (dP - rowsum(P o dP)), dP = dO V^T */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i)
+            grad_score_row(P + i * N, doh + i * d, vh, N, d, dS + i * N);
+        /* dQ = scale * dS K */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            for (long t = 0; t < d; ++t) {
+                double acc = 0.0;
+                for (long j = 0; j < N; ++j)
+                    acc += dS[i * N + j] * kh[j * d + t];
+                dqh[i * d + t] = scale * acc;
+            }
+        }
+        /* dK = scale * dS^T Q and dV = P^T dO, one key j at a time */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (long j = 0; j < N; ++j) {
+            for (long t = 0; t < d; ++t) {
+                double ak = 0.0, av = 0.0;
+                for (long i = 0; i < N; ++i) {
+                    ak += dS[i * N + j] * qh[i * d + t];
+                    av += P[i * N + j] * doh[i * d + t];
+                }
+                dkh[j * d + t] = scale * ak;
+                dvh[j * d + t] = av;
+            }
+        }
+    }
+    free(P);
+    free(dS);
+    return 0;
+}
+
+/* dQ for chosen rows only (triples (b, h, i) in rows): the same definition,
+ * one score row at a time, so that single rows of very large problems can be
+ * checked.  dq_rows is [nrows, d].  Returns 0, or -1 on a bad index or when
+ * memory runs out. */
+int oracle_attention_backward_dq_rows(const double *q, const double *k, const double *v,
+                                      const double *dout, long B, long H, long N,
+                                      long d, double scale, int causal, const long *rows,
+                                      long nrows, double *dq_rows)
+{
+    for (long r = 0; r < nrows; ++r) {
+        long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N)
+            return -1;
+    }
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        double *p = (double *)malloc((size_t)N * sizeof(double));
+        if (!s || !p) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < nrows; ++r) {
+            if (!s || !p)
+                continue;
+            long b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            long bh = b * H + h;
+            const double *kh = k + bh * N * d;
+            score_row(q + (bh * N + i) * d, kh, i, N, d, scale, causal, s);
+            oracle_softmax(s, N, p);
+            grad_score_row(p, dout + (bh * N + i) * d, v + bh * N * d, N, d, s);
+            for (long t = 0; t < d; ++t) {
+                double acc = 0.0;
+                for (long j = 0; j < N; ++j)
+                    acc += s[j] * kh[j * d + t];
+                dq_rows[r * d + t] = scale * acc;
+            }
         }
         free(s);
         free(p);

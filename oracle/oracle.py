@@ -1,4 +1,5 @@
-"""ctypes front end of the fp64 CPU oracle in ``oracle.c``.
+"""ctypes front end of the fp64 CPU oracle in ``oracle.c`` (forward pass and
+its gradients).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module.  It shares no code with
@@ -75,6 +76,12 @@ class Oracle:
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = [_D, _D, _D] + [ctypes.c_long] * 4 + [
             ctypes.c_double, ctypes.c_int, _L, ctypes.c_long, _D, _D]
+        lib.oracle_attention_backward.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = [_D, _D, _D, _D] + [ctypes.c_long] * 4 + [
+            ctypes.c_double, ctypes.c_int, _D, _D, _D]
+        lib.oracle_attention_backward_dq_rows.restype = ctypes.c_int
+        lib.oracle_attention_backward_dq_rows.argtypes = [_D, _D, _D, _D] + [ctypes.c_long] * 4 + [
+            ctypes.c_double, ctypes.c_int, _L, ctypes.c_long, _D]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         self._lib = lib
@@ -127,6 +134,42 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_attention_rows: bad row index or out of memory")
         return o, lse
+
+    # -- backward (gradients of the forward definition) ----------------------
+    def attention_backward(self, q, k, v, dout, scale: float, causal: bool):
+        """q, k, v, dout: [B, H, N, d] (or [N, d]).  Returns (dQ, dK, dV) of
+        the forward definition for the output gradient ``dout``, in float64."""
+        q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+        squeeze = q.ndim == 2
+        if squeeze:
+            q, k, v, dout = q[None, None], k[None, None], v[None, None], dout[None, None]
+        if not (q.shape == k.shape == v.shape == dout.shape and q.ndim == 4):
+            raise ValueError("q, k, v, dout must share one [B,H,N,d] shape")
+        B, H, N, d = q.shape
+        dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+        rc = self._lib.oracle_attention_backward(
+            _dptr(q), _dptr(k), _dptr(v), _dptr(dout), B, H, N, d, float(scale),
+            int(bool(causal)), _dptr(dq), _dptr(dk), _dptr(dv))
+        if rc != 0:
+            raise MemoryError("oracle_attention_backward: out of memory")
+        if squeeze:
+            return dq[0, 0], dk[0, 0], dv[0, 0]
+        return dq, dk, dv
+
+    def attention_backward_dq_rows(self, q, k, v, dout, scale: float, causal: bool, rows):
+        """rows: int array [R, 3] of (b, h, i).  Returns dQ rows [R, d]."""
+        q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+        if not (q.shape == k.shape == v.shape == dout.shape and q.ndim == 4):
+            raise ValueError("q, k, v, dout must share one [B,H,N,d] shape")
+        B, H, N, d = q.shape
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        out = np.empty((r.shape[0], d), dtype=np.float64)
+        rc = self._lib.oracle_attention_backward_dq_rows(
+            _dptr(q), _dptr(k), _dptr(v), _dptr(dout), B, H, N, d, float(scale),
+            int(bool(causal)), r.ctypes.data_as(_L), r.shape[0], _dptr(out))
+        if rc != 0:
+            raise ValueError("oracle_attention_backward_dq_rows: bad row index or out of memory")
+        return out
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())

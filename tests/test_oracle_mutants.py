@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from oracle import oracle as oracle_mod
-from tests import pins
+from tests import pins, pins_bwd
 
 MUTANTS = {
     "dot_wrong_index": ("dot += q_row[t] * k_row[t];", "dot += q_row[t] * k_row[(t + 1) % d];"),
@@ -37,6 +37,26 @@ MUTANTS = {
                            "score_row(qh + (i ? i - 1 : 0) * d, kh, i, N, d, scale, causal, S + i * N);"),
 }
 
+# Planted mistakes in the backward pass; each must fail a backward pin.
+BWD_MUTANTS = {
+    "bwd_drops_rowsum": ("ds[j] = p[j] * (ds[j] - dsum);", "ds[j] = p[j] * ds[j];"),
+    "bwd_rowsum_sign": ("ds[j] = p[j] * (ds[j] - dsum);", "ds[j] = p[j] * (dsum - ds[j]);"),
+    "bwd_rowsum_unweighted": ("dsum += p[j] * dp;", "dsum += dp;"),
+    "bwd_do_row_shifted": ("grad_score_row(P + i * N, doh + i * d, vh, N, d, dS + i * N);",
+                           "grad_score_row(P + i * N, doh + ((i + 1) % N) * d, vh, N, d, dS + i * N);"),
+    "bwd_dp_wrong_index": ("dp += do_row[t] * v_row[t];", "dp += do_row[t] * v_row[(t + 1) % d];"),
+    "bwd_dq_no_scale": ("dqh[i * d + t] = scale * acc;", "dqh[i * d + t] = acc;"),
+    "bwd_dq_uses_q": ("acc += dS[i * N + j] * kh[j * d + t];", "acc += dS[i * N + j] * qh[j * d + t];"),
+    "bwd_dq_transposed_ds": ("acc += dS[i * N + j] * kh[j * d + t];", "acc += dS[j * N + i] * kh[j * d + t];"),
+    "bwd_dk_uses_p": ("ak += dS[i * N + j] * qh[i * d + t];", "ak += P[i * N + j] * qh[i * d + t];"),
+    "bwd_dk_transposed_ds": ("ak += dS[i * N + j] * qh[i * d + t];", "ak += dS[j * N + i] * qh[i * d + t];"),
+    "bwd_dk_no_scale": ("dkh[j * d + t] = scale * ak;", "dkh[j * d + t] = ak;"),
+    "bwd_dv_uses_ds": ("av += P[i * N + j] * doh[i * d + t];", "av += dS[i * N + j] * doh[i * d + t];"),
+    "bwd_dv_transposed_p": ("av += P[i * N + j] * doh[i * d + t];", "av += P[j * N + i] * doh[i * d + t];"),
+    "bwd_dv_uses_v": ("av += P[i * N + j] * doh[i * d + t];", "av += P[i * N + j] * vh[i * d + t];"),
+    "bwd_rows_wrong_index": ("acc += s[j] * kh[j * d + t];", "acc += s[j] * kh[j * d + (t + 1) % d];"),
+}
+
 
 def _build_mutant(tmp_path, name, old, new):
     src = open(oracle_mod.SRC).read()
@@ -57,6 +77,19 @@ def test_mutant_is_caught(name, tmp_path):
     for pin in pins.ALL_PINS:
         try:
             pin(o)
-        except (AssertionError, ValueError, FloatingPointError) as e:
+        except (AssertionError, ValueError, FloatingPointError):
             failures.append(pin.__name__)
     assert failures, f"planted mistake {name!r} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    o = _build_mutant(tmp_path, name, old, new)
+    failures = []
+    for pin in pins_bwd.BWD_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, FloatingPointError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name!r} passed every backward pin"
