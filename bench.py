@@ -7,6 +7,11 @@ Default workload: B=2, H=32, N=8192, d=128, bf16, causal (the configuration
 the MFMA-peak target is stated for).  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--pass fwd|bwd]
+
+--pass bwd times the backward pass instead (one step = one fa_bwd call: the
+dq kernel and the dkdv kernel) with the nominal backward FLOPs
+10*B*H*N^2*d (five N x N x d products), halved under the causal mask.
 
 FLOPs are the nominal matmul count 4*B*H*N^2*d, halved under the causal
 mask.  `roofline` reports the kernel's own average launch duration, measured
@@ -42,13 +47,14 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU * 2.4 GHz * 4096 FL
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (used only for fp32 workloads)
 KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_fwd_bf16.hip",
                   "exact_attention_32_amd/csrc/fa_fwd_f32.hip"]
+BWD_KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_bwd_bf16.hip"]
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = "profiles/fa_fwd_bf16_b2h32n8192d128_causal_traffic.txt"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -72,6 +78,40 @@ def read_traffic(workload: str):
         return int(fields["HBM_BYTES_PER_LAUNCH"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_baseline_bwd(w, q, k, v, dout, target_s: float):
+    """The oracle's backward pass timed on the host cores on a seeded sample
+    of dQ rows of the same workload.  For each row the oracle forms the
+    score row, the dP row and the dQ row: three of the five products of the
+    backward pass, so FLOPs per row = 3/5 of the workload's backward FLOPs
+    divided by its number of rows."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_32_amd import inputs
+
+    o = oracle.default()
+    qd, kd, vd, dd = (t.float().numpy().astype(np.float64) for t in (q, k, v, dout))
+    per_row = 0.6 * 2.5 * w.flops / (w.B * w.H * w.N)
+    rows = inputs.sample_rows(w, 64, seed=99)
+    t0 = time.perf_counter()
+    o.attention_backward_dq_rows(qd, kd, vd, dd, w.scale, w.causal, rows)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(200000, max(64, 64 * target_s / dt)))
+    rows = inputs.sample_rows(w, n, seed=100)
+    t0 = time.perf_counter()
+    o.attention_backward_dq_rows(qd, kd, vd, dd, w.scale, w.causal, rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n * per_row / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} seeded dQ rows of {w.name} (fp64 definition: score, dP and dQ row "
+                  f"each), {dt:.1f} s; FLOPs per row = 3/5 of the workload's backward "
+                  f"FLOPs / rows",
+    }
 
 
 def cpu_baseline(w, q, k, v, target_s: float):
@@ -122,6 +162,7 @@ def summarize_trace(directory: str, command: str) -> None:
     run (SQLite output under `directory`)."""
     print(f"COMMAND: {command}")
     print("KERNEL_SOURCE_SHA256_16:", kernel_source_hash())
+    print("BWD_KERNEL_SOURCE_SHA256_16:", kernel_source_hash(BWD_KERNEL_SOURCES))
     print("kernel | calls | total_ms | average_us | percent")
     for name, calls, total, avg, pct in _db_rows(
             directory, "select name, total_calls, total_duration, average, percentage "
@@ -169,6 +210,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -204,11 +246,30 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)   # default priority
     fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+    flops = w.flops
 
     def step():
         rc = fn(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, stream)
         if rc != fa.FA_OK:
             raise fa.FAError(rc, fa.fa_strerror(rc))
+
+    if args.which == "bwd":
+        if w.dtype != "bf16":
+            raise SystemExit("the backward pass is bf16 only")
+        dout = inputs.make_dout(w)
+        dd = dout.to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+        delta = torch.empty_like(lse)
+        with torch.cuda.stream(stream):
+            step()                        # the forward pass's O and LSE
+        torch.cuda.synchronize(dev)
+        flops = 2.5 * w.flops
+
+        def step():  # noqa: F811
+            rc = fa.fa_bwd(qd, kd, vd, o, dd, lse, dq, dk, dv, delta, w.B, w.H, w.N, w.d,
+                           w.scale, w.causal, stream)
+            if rc != fa.FA_OK:
+                raise fa.FAError(rc, fa.fa_strerror(rc))
 
     torch.cuda.synchronize(dev)
     if args.copy_calibration:
@@ -240,11 +301,14 @@ def main() -> int:
     kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
     ms_per_step = wall * 1e3 / args.steps
 
-    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    metric = "attention fwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
+    if args.which == "bwd":
+        metric = "attention bwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
     line = {
-        "metric": "attention fwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -257,15 +321,19 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "inputs": w.dist, "flops_per_step": w.flops,
+                   "causal": w.causal, "inputs": w.dist, "pass": args.which,
+                   "flops_per_step": flops,
                    "pct_mfma_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": read_traffic(w.name),
+                     "traffic": read_traffic(w.name) if args.which == "fwd" else None,
                      "kernel_ms": round(kernel_ms, 4)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        if args.which == "bwd":
+            line["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout, args.cpu_seconds)
+        else:
+            line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 

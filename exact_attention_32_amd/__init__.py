@@ -1,10 +1,11 @@
-"""MI355X (gfx950) exact attention forward pass.
+"""MI355X (gfx950) exact attention forward and backward pass.
 
 O = softmax(scale * Q K^T [+ causal mask]) V and the per-row log-sum-exp,
-computed tile by tile in hand-written HIP kernels behind the C ABI of
-``include/fa.h``.  This package is the thin Python binding of that library
-(``fa_fwd``, ``fa_fwd_f32``, ``fa_strerror`` with the C names, plus the torch
-convenience ``forward``) and the seeded input generators in ``inputs``.
+and the gradients dQ, dK, dV, computed tile by tile in hand-written HIP
+kernels behind the C ABI of ``include/fa.h``.  This package is the thin Python
+binding of that library (``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``,
+``fa_strerror`` with the C names, plus the torch conveniences ``forward`` and
+``backward``) and the seeded input generators in ``inputs``.
 """
 from ._lib import (  # noqa: F401
     EXPORTS,
@@ -18,6 +19,8 @@ from ._lib import (  # noqa: F401
     FA_OK,
     LIB_PATH,
     FAError,
+    backward,
+    fa_bwd,
     fa_fwd,
     fa_fwd_f32,
     fa_strerror,

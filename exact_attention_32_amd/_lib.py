@@ -1,4 +1,4 @@
-"""ctypes binding of libfa (include/fa.h).  Argument marshalling only: every
+"""ctypes binding of libfa (include/fa.h): forward and backward pass.  Argument marshalling only: every
 step of the computation runs in the HIP kernels of the library.
 
 There is no fallback: if ``libfa.so`` has not been built, or cannot be
@@ -22,7 +22,7 @@ FA_ERR_ALIGN = 5
 FA_ERR_HIP = 6
 FA_ERR_ALIAS = 7
 
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror")
+EXPORTS = ("fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_strerror")
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = i
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [i]
     _lib = lib
@@ -89,6 +91,16 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
                                          int(bool(causal)), _stream(stream)))
 
 
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal,
+           stream=None) -> int:
+    """Enqueue the bf16 backward pass; pointers may be ints or tensors.
+    Returns the fa_status code (0 on success)."""
+    return int(load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                     _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                     int(B), int(H), int(N), int(d), float(scale),
+                                     int(bool(causal)), _stream(stream)))
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
             stream=None):
     """Torch convenience wrapper: q, k, v are contiguous [B, H, N, d] device
@@ -120,3 +132,37 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             stream=None):
+    """Torch convenience wrapper of fa_bwd: q, k, v, o, dout are contiguous
+    bf16 [B, H, N, d] device tensors and (o, lse) what ``forward`` returned
+    for q, k, v with the same causal and scale.  Allocates dQ, dK, dV (bf16)
+    and the fp32 [B, H, N] workspace delta, enqueues the two kernels on
+    ``stream`` (default: the current torch stream) and returns
+    (dQ, dK, dV, delta)."""
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if not (all(t.shape == q.shape for t in ts) and q.dim() == 4):
+        raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
+    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
+        raise TypeError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if not all(t.is_cuda for t in ts + (lse,)):
+        raise ValueError("all tensors must be device tensors")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return dq, dk, dv, delta

@@ -37,6 +37,35 @@ int validate(const void *q, const void *k, const void *v, const void *o, const v
     return FA_OK;
 }
 
+// fa_bwd: the shared checks of `validate` on the forward quantities, then
+// the extra pointers and their aliasing.
+int validate_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const void *lse, const void *dq, const void *dk, const void *dv,
+                 const void *delta, int B, int H, int N, int d, float scale) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    for (const void *p : {q, k, v, o, dout, lse, dq, dk, dv, delta})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    const uint64_t rows = bh * (uint64_t)N;
+    const uint64_t t_bytes = rows * (uint64_t)d * 2u;
+    const uint64_t l_bytes = rows * 4u;
+    struct Span { const void *p; uint64_t n; };
+    const Span ins[] = {{q, t_bytes}, {k, t_bytes}, {v, t_bytes}, {o, t_bytes},
+                        {dout, t_bytes}, {lse, l_bytes}};
+    const Span outs[] = {{dq, t_bytes}, {dk, t_bytes}, {dv, t_bytes}, {delta, l_bytes}};
+    for (const Span &w : outs)
+        for (const Span &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_ALIAS;
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +88,16 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H, int N,
+           int d, float scale, int causal, hipStream_t stream) {
+    const int rc = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
+                                             d, scale, causal != 0, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char *fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";
@@ -68,7 +107,7 @@ const char *fa_strerror(int status) {
         case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
         case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";
-        case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o or lse overlaps an input or each other";
+        case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
         default: return "unknown fa status code";
     }
 }

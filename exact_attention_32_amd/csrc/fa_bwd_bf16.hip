@@ -1,0 +1,539 @@
+// fa_bwd_bf16.hip -- backward pass of the fused attention for gfx950: bf16
+// Q, K, V, O, dO in; bf16 dQ, dK, dV out; fp32 scores, probabilities and
+// accumulators.
+//
+// What is computed: the gradients of O = softmax(scale * Q K^T [+ causal
+// mask]) V for an output gradient dO.  The pages describe the backward pass
+// only as recomputation: S and P are rebuilt tile by tile from Q, K and the
+// row statistics the forward pass kept, never stored as N x N matrices
+// ("解析 FlashAttention（2）", section 1.2 (3), and the note after Algorithm 1
+// that m and l are kept for the backward pass; the unit-12 lesson on memory;
+// the Triton page, section 5.1: dQ, dK and dV, blocked and accumulated online).
+// The per-tile formulas are the chain rule through P = softmax(S):
+//   P_ij  = exp(scale * q_i.k_j - LSE_i)         (LSE from the forward pass)
+//   dP_ij = dO_i . v_j
+//   D_i   = sum_j P_ij dP_ij = dO_i . O_i
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dV_j += P_ij dO_i,  dK_j += scale dS_ij q_i,  dQ_i += scale dS_ij k_j
+//
+// Two kernels, both on v_mfma_f32_32x32x16_bf16 with the operand layouts of
+// the forward kernel (a lane owns one query or one key of a 32 x 32 block):
+//  * dq kernel (query tiles outside, key tiles inside, like the forward):
+//    computes D_i for its rows first and stores it for the second kernel;
+//    then per 64-key tile S^T = K Q^T and dP^T = V dO^T, dS^T, and
+//    dQ^T += K^T dS^T, where K^T comes out of the K tile through the LDS
+//    transpose read.
+//  * dkdv kernel (key tiles outside, query tiles inside): per 64-query tile
+//    S = Q K^T and dP = dO V^T (Q, dO from LDS, K, V in registers), then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+// Staging is the forward's: 16-byte direct-to-LDS buffer loads, double
+// buffered, rows past N arriving as zeros; every tile that is read both
+// row-wise and transposed uses one XOR swizzle that keeps both read patterns
+// free of bank conflicts.  Causal: key tiles wholly after a query tile (or
+// query tiles wholly before a key tile) are never visited; only tiles that
+// straddle the diagonal or the ragged end of N pay for the element mask.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+#define LDS3 __attribute__((address_space(3)))
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;            // queries (dq) or keys (dkdv) per wave
+constexpr int kOuter = kWaves * kRowsPerWave;  // rows owned by one workgroup
+constexpr int kInner = 64;                  // rows per streamed tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One swizzle for tiles read both by 128-bit row reads (16 rows x one 16-byte
+// chunk per LDS pass) and by the 64-bit transpose read (4 rows x 4 chunks per
+// pass): the stored chunk of logical chunk c in row r is c ^ swz(r).
+//   d = 128 (one row per 256-byte line): swz = 4(r & 3) + ((r >> 2) & 3);
+//   d = 64  (two rows per line):         swz = 4((r >> 1) & 1) + ((r >> 2) & 3).
+// Both depend on r mod 16 only.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Workgroup id -> (batch*head, tile): consecutive ids go to consecutive XCDs,
+// and XCD x walks the contiguous range [x*W/8, (x+1)*W/8) of (head, tile)
+// pairs when the grid divides evenly (its L2 then serves one head's stream).
+__device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse, int &bh,
+                                          int &tile) {
+    int gidx = L;
+    if ((W & 7) == 0) gidx = (L & 7) * (W >> 3) + (L >> 3);
+    bh = gidx / ntiles;
+    tile = gidx - bh * ntiles;
+    if (reverse) tile = ntiles - 1 - tile;
+}
+
+// Direct-to-LDS copy of one kInner-row tile of a [N, D] bf16 matrix (rows r0
+// .. r0 + kInner - 1; rows >= N read as zeros) into `dst`, swizzled: lane l of
+// load u of wave w writes chunk position q = (u*kWaves + w)*64 + l, and
+// fetches the logical chunk that the swizzle stores there (`src[u]`).
+template <int D>
+__device__ __forceinline__ void load_tile(const __bf16 *mat, int N, int r0, LDS3 char *dst,
+                                          const uint32_t *src, int wave) {
+    constexpr int kLoads = kInner * (D / 8) / kThreads;
+    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - r0)) * (uint32_t)(D * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat + (size_t)r0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)(dst + (u * kWaves + wave) * 1024),
+                                                 16, src[u], 0, 0, 0);
+}
+
+// Direct-to-LDS copy of vec[c0 .. c0 + 63] (fp32; entries at or past N read
+// as 0) into dst[0 .. 63], one 4-byte load per lane of the calling wave.
+__device__ __forceinline__ void load_vec(const float *vec, int N, int c0, LDS3 float *dst,
+                                         int lane) {
+    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - c0)) * 4u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vec + c0, bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
+}
+
+// Lane-constant source offsets of load_tile (see there).
+template <int D>
+__device__ __forceinline__ void tile_src_offsets(int wave, int lane, uint32_t *src) {
+    constexpr int kLoads = kInner * (D / 8) / kThreads;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int q = (u * kWaves + wave) * 64 + lane;
+        const int r = q / (D / 8);
+        const int p = q % (D / 8);
+        src[u] = (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
+    }
+}
+
+// Byte offsets (within a tile) of the 128-bit operand reads: lane (g, i) reads
+// row i (+32 per 32-row block) and logical chunk 2ks + g.
+template <int D>
+__device__ __forceinline__ void row_read_offsets(int lane, uint32_t *off) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) off[ks] = (uint32_t)(i * D * 2 + (((2 * ks + g) ^ swz<D>(i)) << 4));
+}
+
+// Byte offsets of the transpose reads that form the A operand M^T (M = a
+// tile, [row][d]) of a 32 (d) x 16 (rows) MFMA block: in 16-lane group
+// G = lane/16 (m0 = 16 (G & 1), g = G >> 1), lane i of the group reads the
+// four bf16 of row 16T + 8h + 4g + i/4, columns 32db + m0 + 4(i%4) .. +3; the
+// two halves h = 0, 1 form one 8-element operand.  The swizzle term depends on
+// h (not on T), so each h has its own offsets.
+template <int D>
+__device__ __forceinline__ void tr_read_offsets(int lane, uint32_t (*off)[D / 32]) {
+    const int g = lane >> 5, gi = lane & 15, m0 = 16 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int row = 8 * h + 4 * g + (gi >> 2);
+            const int col = 32 * db + m0 + 4 * (gi & 3);
+            const int c = col >> 3;
+            off[h][db] = (uint32_t)(row * D * 2 + ((c ^ swz<D>(row)) << 4) + ((col & 4) << 1));
+        }
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 tr_read(const LDS3 char *tile, const uint32_t (*off)[D / 32],
+                                          int T, int db) {
+    const LDS3 char *base = tile + T * 16 * D * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + off[0][db]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + off[1][db]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ u32x4 load16(const __bf16 *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Store a [D x 32] accumulator block set (lane (g, j) holds row `row` of the
+// result, columns 32db + 8a + 4g + e in acc[db][4a + e]) times `mul` as bf16.
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, float mul, int g) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * mul;
+            *reinterpret_cast<bf16x4 *>(row_ptr + 32 * db + 8 * a + 4 * g) =
+                __builtin_convertvector(x, bf16x4);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dq kernel: one workgroup = 128 queries of one (batch, head); wave w owns
+// queries r0 + 32w .. +31 (lane (g, j) holds query j of the wave).
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
+              const __bf16 *__restrict__ V, const __bf16 *__restrict__ O,
+              const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
+              float *__restrict__ Delta, __bf16 *__restrict__ dQ, int N, int ntiles,
+              float scale, float scale_log2) {
+    constexpr int kLoads = kInner * (D / 8) / kThreads;
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k0[kInner * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k1[kInner * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v0[kInner * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v1[kInner * D];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int g = lane >> 5;
+    const int j = lane & 31;
+
+    int bh, qt;
+    map_block(blockIdx.x, gridDim.x, ntiles, CAUSAL, bh, qt);
+    const int r0 = qt * kOuter;
+    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const __bf16 *Kh = K + hoff;
+    const __bf16 *Vh = V + hoff;
+    const int wrow0 = r0 + wave * kRowsPerWave;
+    const int qrow = wrow0 + j;
+    const bool valid = qrow < N;
+
+    // Q^T and dO^T as B operands: lane (g, j) holds columns 16ks+8g..+7 of
+    // its query row.  D_i = dO_i . O_i from the same columns, then summed
+    // over the two half-waves.
+    bf16x8 qop[D / 16], doop[D / 16];
+    float dpart = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
+        if (valid) {
+            const size_t e = hoff + (size_t)qrow * D + 16 * ks + 8 * g;
+            xq = load16(Q + e);
+            xd = load16(dO + e);
+            xo = load16(O + e);
+        }
+        qop[ks] = __builtin_bit_cast(bf16x8, xq);
+        doop[ks] = __builtin_bit_cast(bf16x8, xd);
+        const bf16x8 ov = __builtin_bit_cast(bf16x8, xo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)doop[ks][e], (float)ov[e], dpart);
+    }
+    float delta;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart),
+                                                         __float_as_uint(dpart), false, false);
+        delta = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (valid && g == 0) Delta[(size_t)bh * N + qrow] = delta;
+    const float lse2 = valid ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+
+    const int kv_end = CAUSAL ? min(N, r0 + kOuter) : N;
+    const int n_tiles = (kv_end + kInner - 1) / kInner;
+
+    uint32_t src[kLoads];
+    tile_src_offsets<D>(wave, lane, src);
+    uint32_t rd[D / 16];
+    row_read_offsets<D>(lane, rd);
+    uint32_t trd[2][D / 32];
+    tr_read_offsets<D>(lane, trd);
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    LDS3 char *const k0 = (LDS3 char *)lds_k0;
+    LDS3 char *const k1 = (LDS3 char *)lds_k1;
+    LDS3 char *const v0 = (LDS3 char *)lds_v0;
+    LDS3 char *const v1 = (LDS3 char *)lds_v1;
+
+    auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk, LDS3 char *nv) {
+        const int c0 = t * kInner;
+        if (t + 1 < n_tiles) {
+            load_tile<D>(Kh, N, c0 + kInner, nk, src, wave);
+            load_tile<D>(Vh, N, c0 + kInner, nv, src, wave);
+        }
+        const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
+        if (active) {
+            // S^T = K Q^T and dP^T = V dO^T (keys x queries).
+            f32x16 s[kInner / 32], dp[kInner / 32];
+#pragma unroll
+            for (int kb = 0; kb < kInner / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < kInner / 32; ++kb) {
+                    const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(kt + rd[ks] + kb * 32 * D * 2);
+                    const bf16x8 vf = *reinterpret_cast<const LDS3 bf16x8 *>(vt + rd[ks] + kb * 32 * D * 2);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qop[ks], s[kb], 0, 0, 0);
+                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, doop[ks], dp[kb], 0, 0, 0);
+                }
+            // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
+            const bool need_mask = (CAUSAL && c0 + kInner - 1 > wrow0) || (c0 + kInner > N);
+            if (need_mask) {
+                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - c0 - 4 * g;
+#pragma unroll
+                for (int kb = 0; kb < kInner / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+            }
+            // dS^T = P^T o (dP^T - D), rounded to bf16 as the B operand of
+            // the next product (rows 0-7 / 8-15 of a block are two k-steps).
+            bf16x8 dsop[kInner / 16];
+#pragma unroll
+            for (int kb = 0; kb < kInner / 32; ++kb) {
+                f32x8 lo, hi;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float plo = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
+                    const float phi = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 8], scale_log2, -lse2));
+                    lo[r] = plo * (dp[kb][r] - delta);
+                    hi[r] = phi * (dp[kb][r + 8] - delta);
+                }
+                dsop[2 * kb] = __builtin_convertvector(lo, bf16x8);
+                dsop[2 * kb + 1] = __builtin_convertvector(hi, bf16x8);
+            }
+            // dQ^T += K^T dS^T; k-step T covers keys 16T .. 16T+15.
+#pragma unroll
+            for (int T = 0; T < kInner / 16; ++T)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(kt, trd, T, db),
+                                                                      dsop[T], acc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    load_tile<D>(Kh, N, 0, k0, src, wave);
+    load_tile<D>(Vh, N, 0, v0, src, wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, k0, v0, k1, v1);
+        if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
+    }
+    if (valid) store_rows<D>(dQ + hoff + (size_t)qrow * D, acc, scale, g);
+}
+
+// ---------------------------------------------------------------------------
+// dkdv kernel: one workgroup = 128 keys of one (batch, head); wave w owns
+// keys k0 + 32w .. +31 (lane (g, j) holds key j of the wave).  Query tiles
+// of 64 rows stream through LDS together with their LSE and D values.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
+                const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
+                const float *__restrict__ LSE, const float *__restrict__ Delta,
+                __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, int ntiles,
+                float scale, float scale_log2) {
+    constexpr int kLoads = kInner * (D / 8) / kThreads;
+    __shared__ __attribute__((aligned(16))) __bf16 lds_q0[kInner * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_q1[kInner * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_o0[kInner * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_o1[kInner * D];
+    // per tile: LSE (log2 units are formed on read) then D, 64 floats each
+    __shared__ __attribute__((aligned(16))) float lds_s0[2 * kInner];
+    __shared__ __attribute__((aligned(16))) float lds_s1[2 * kInner];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int g = lane >> 5;
+    const int j = lane & 31;
+
+    int bh, kt;
+    // Under the causal mask the first key tiles see the most queries: they
+    // are issued first (no reversal).
+    map_block(blockIdx.x, gridDim.x, ntiles, false, bh, kt);
+    const int k0 = kt * kOuter;
+    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const __bf16 *Qh = Q + hoff;
+    const __bf16 *dOh = dO + hoff;
+    const float *LSEh = LSE + (size_t)bh * N;
+    const float *Dh = Delta + (size_t)bh * N;
+    const int wk0 = k0 + wave * kRowsPerWave;
+    const int key = wk0 + j;
+    const bool valid = key < N;
+
+    // K^T and V^T as B operands: lane (g, j) holds columns 16ks+8g..+7 of its key.
+    bf16x8 kop[D / 16], vop[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        if (valid) {
+            const size_t e = hoff + (size_t)key * D + 16 * ks + 8 * g;
+            xk = load16(K + e);
+            xv = load16(V + e);
+        }
+        kop[ks] = __builtin_bit_cast(bf16x8, xk);
+        vop[ks] = __builtin_bit_cast(bf16x8, xv);
+    }
+
+    // Causal: the query tiles before the workgroup's first key see none of its keys.
+    const int t_begin = CAUSAL ? k0 / kInner : 0;
+    const int n_tiles = (N + kInner - 1) / kInner;
+
+    uint32_t src[kLoads];
+    tile_src_offsets<D>(wave, lane, src);
+    uint32_t rd[D / 16];
+    row_read_offsets<D>(lane, rd);
+    uint32_t trd[2][D / 32];
+    tr_read_offsets<D>(lane, trd);
+
+    f32x16 acck[D / 32], accv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acck[db][r] = accv[db][r] = 0.f;
+
+    LDS3 char *const q0 = (LDS3 char *)lds_q0;
+    LDS3 char *const q1 = (LDS3 char *)lds_q1;
+    LDS3 char *const o0 = (LDS3 char *)lds_o0;
+    LDS3 char *const o1 = (LDS3 char *)lds_o1;
+
+    // Rows c0 .. c0+63 of Q and dO, and their LSE and D (waves 0 and 1 copy
+    // those, one 4-byte direct-to-LDS load each; entries past N read as 0).
+    auto load_all = [&](int c0, LDS3 char *dq_, LDS3 char *do_, LDS3 float *st) {
+        load_tile<D>(Qh, N, c0, dq_, src, wave);
+        load_tile<D>(dOh, N, c0, do_, src, wave);
+        if (wave < 2) load_vec(wave == 0 ? LSEh : Dh, N, c0, st + wave * kInner, lane);
+    };
+
+    auto step = [&](int t, const LDS3 char *qt_, const LDS3 char *ot_, const LDS3 float *st,
+                    LDS3 char *nq, LDS3 char *no, LDS3 float *nst) {
+        const int c0 = t * kInner;
+        if (t + 1 < n_tiles) load_all(c0 + kInner, nq, no, nst);
+        // A wave whose keys all follow this query tile has nothing to add.
+        const bool active = !CAUSAL || c0 + kInner - 1 >= wk0;
+        if (active) {
+            // Two halves of 32 queries; element r of a half's block is query
+            // c0 + 32qb + 8(r/4) + 4g + r%4 (and the lane's key).
+#pragma unroll
+            for (int qb = 0; qb < kInner / 32; ++qb) {
+                f32x16 s = {}, dp = {};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bf16x8 qf = *reinterpret_cast<const LDS3 bf16x8 *>(qt_ + rd[ks] + qb * 32 * D * 2);
+                    const bf16x8 of = *reinterpret_cast<const LDS3 bf16x8 *>(ot_ + rd[ks] + qb * 32 * D * 2);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kop[ks], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vop[ks], dp, 0, 0, 0);
+                }
+                const int qbase = c0 + 32 * qb;
+                const bool need_mask = (CAUSAL && qbase < wk0 + kRowsPerWave - 1) || (qbase + 32 > N);
+                if (need_mask) {
+                    // visible iff query >= key (causal) and query < N
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qi = qbase + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if (qi >= N || (CAUSAL && qi < key)) s[r] = -INFINITY;
+                    }
+                }
+                f32x8 plo, phi, dlo, dhi;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 l4 = *reinterpret_cast<const LDS3 f32x4 *>(st + 32 * qb + 8 * a + 4 * g);
+                    const f32x4 d4 = *reinterpret_cast<const LDS3 f32x4 *>(st + kInner + 32 * qb + 8 * a + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * a + e;
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -l4[e] * kLog2e));
+                        const float ds = p * (dp[r] - d4[e]);
+                        if (r < 8) { plo[r] = p; dlo[r] = ds; }
+                        else { phi[r - 8] = p; dhi[r - 8] = ds; }
+                    }
+                }
+                const bf16x8 pop[2] = {__builtin_convertvector(plo, bf16x8), __builtin_convertvector(phi, bf16x8)};
+                const bf16x8 dsop[2] = {__builtin_convertvector(dlo, bf16x8), __builtin_convertvector(dhi, bf16x8)};
+                // dV^T += dO^T P and dK^T += Q^T dS over the half's 32 queries
+                // (k-steps T = 2qb, 2qb + 1).
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(ot_, trd, 2 * qb + h, db),
+                                                                           pop[h], accv[db], 0, 0, 0);
+                        acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(qt_, trd, 2 * qb + h, db),
+                                                                           dsop[h], acck[db], 0, 0, 0);
+                    }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    LDS3 float *const s0 = (LDS3 float *)lds_s0;
+    LDS3 float *const s1 = (LDS3 float *)lds_s1;
+    if (t_begin < n_tiles) {
+        load_all(t_begin * kInner, q0, o0, s0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int t = t_begin; t < n_tiles; t += 2) {
+            step(t, q0, o0, s0, q1, o1, s1);
+            if (t + 1 < n_tiles) step(t + 1, q1, o1, s1, q0, o0, s0);
+        }
+    }
+    if (valid) {
+        store_rows<D>(dK + hoff + (size_t)key * D, acck, scale, g);
+        store_rows<D>(dV + hoff + (size_t)key * D, accv, 1.f, g);
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+                  int N, float scale, hipStream_t stream) {
+    const int ntiles = (N + kOuter - 1) / kOuter;
+    const int blocks = B * H * ntiles;
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+    const __bf16 *Q = static_cast<const __bf16 *>(q), *K = static_cast<const __bf16 *>(k),
+                 *V = static_cast<const __bf16 *>(v), *O = static_cast<const __bf16 *>(o),
+                 *dO = static_cast<const __bf16 *>(dout);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream, Q, K,
+                       V, O, dO, lse, delta, static_cast<__bf16 *>(dq), N, ntiles, scale,
+                       scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream, Q,
+                       K, V, dO, lse, delta, static_cast<__bf16 *>(dk), static_cast<__bf16 *>(dv),
+                       N, ntiles, scale, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
+                           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                           float *delta, int B, int H, int N, int d, float scale, bool causal,
+                           hipStream_t stream) {
+    if (d == 64)
+        return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream)
+                      : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream);
+    return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream)
+                  : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream);
+}
+
+}  // namespace fa

@@ -16,4 +16,11 @@ hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float 
                           float *lse, int B, int H, int N, int d, float scale,
                           bool causal, hipStream_t stream);
 
+// Backward pass: enqueues the dq kernel (which also writes delta) and then the
+// dkdv kernel on `stream`.
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
+                           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                           float *delta, int B, int H, int N, int d, float scale, bool causal,
+                           hipStream_t stream);
+
 }  // namespace fa

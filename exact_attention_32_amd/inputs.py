@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module is the only code shared by the tests, the benchmark and the
 oracle side: it draws numbers and knows the workload shapes, and holds none of
@@ -12,6 +12,9 @@ the storage dtype by round-to-nearest-even):
 * ``normal4`` -- Q and K i.i.d. N(0, 4^2) (``4 * torch.randn``), V N(0, 1);
   large logits whose row maxima move from tile to tile;
 * ``uniform`` -- i.i.d. U(-1, 1) (``2 * torch.rand - 1``).
+
+The output gradient dO of the backward pass is drawn from its own generator
+(seed + 10000), i.i.d. N(0, 1), rounded to bf16 (``make_dout``).
 
 ``scale`` is the fp32 value of 1/sqrt(d).  The pages measure on no public
 dataset: every input is synthetic and shaped like the pages' workloads
@@ -93,6 +96,15 @@ def make_qkv(w: Workload, device="cpu"):
     v = draw(False)
     dt = torch_dtype(w.dtype)
     return tuple(t.to(dt).contiguous().to(device) for t in (q, k, v))
+
+
+def make_dout(w: Workload, device="cpu"):
+    """The output gradient dO for the backward pass: i.i.d. N(0, 1) from a
+    generator seeded with seed + 10000, as fp32 [B, H, N, d] rounded to the
+    workload's storage dtype."""
+    g = torch.Generator("cpu").manual_seed(w.seed + 10000)
+    x = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
+    return x.to(torch_dtype(w.dtype)).contiguous().to(device)
 
 
 def sample_rows(w: Workload, count: int, seed: int = 1234):

@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of libfa, the MI355X (gfx950) exact attention forward pass.
+ * fa.h -- C ABI of libfa, the MI355X (gfx950) exact attention forward pass
+ * and its backward pass.
  *
  *   O   = softmax(scale * Q K^T [+ causal mask]) V
  *   LSE = log-sum-exp of each row of the scaled, masked logits (natural log)
@@ -59,7 +60,7 @@ enum fa_status {
     FA_ERR_SCALE = 4,    /* scale is not finite, or not > 0                  */
     FA_ERR_ALIGN = 5,    /* a pointer is not 16-byte aligned                 */
     FA_ERR_HIP = 6,      /* the kernel launch failed (hipGetLastError)       */
-    FA_ERR_ALIAS = 7     /* o or lse overlaps an input or each other         */
+    FA_ERR_ALIAS = 7     /* an output overlaps an input or another output    */
 };
 
 /*
@@ -84,6 +85,40 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
                float *lse, int B, int H, int N, int d, float scale, int causal,
                hipStream_t stream);
+
+/*
+ * fa_bwd -- gradients of fa_fwd for an output gradient dout: dq = dL/dQ,
+ * dk = dL/dK, dv = dL/dV when dout = dL/dO.
+ *
+ * The pages describe the backward pass as recomputation: the scores and
+ * probabilities are rebuilt tile by tile from Q, K and the row statistics the
+ * forward pass kept, never stored as N x N matrices ("解析 FlashAttention（2）",
+ * section 1.2 (3) and the remark after Algorithm 1 that m and l are kept for
+ * the backward pass; Triton page, section 5.1).  The gradients themselves are
+ * the chain rule through the forward definition:
+ *   P = exp(scale * Q K^T [masked] - LSE),  dV = P^T dout,  dP = dout V^T,
+ *   dS = P o (dP - delta),  delta_i = dout_i . o_i,
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ *   q, k, v : const bf16 [B, H, N, d], the forward pass's inputs
+ *   o       : const bf16 [B, H, N, d], fa_fwd's output for them
+ *   dout    : const bf16 [B, H, N, d]
+ *   lse     : const fp32 [B, H, N], fa_fwd's LSE for the same q, k, v,
+ *             scale and causal
+ *   dq, dk, dv : bf16 [B, H, N, d], written (rounded to nearest even from
+ *             the fp32 accumulators)
+ *   delta   : fp32 [B, H, N], caller-provided workspace; on completion it
+ *             holds delta_i = dout_i . o_i (fp32 sum of bf16 products)
+ * Arithmetic: products on bf16 inputs with fp32 accumulation; P and dS are
+ * rounded to bf16 before they enter the products that need them.
+ * Two kernels are enqueued on `stream` (dq and delta first, then dk and dv).
+ * Shapes, scale, causal, alignment and errors as for fa_fwd; none of dq, dk,
+ * dv, delta may overlap an input or another output (FA_ERR_ALIAS).
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, float *delta,
+           int B, int H, int N, int d, float scale, int causal,
+           hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_strerror(int status);

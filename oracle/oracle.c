@@ -315,6 +315,60 @@ int oracle_attention_backward_dq_rows(const double *q, const double *k, const do
     return failed ? -1 : 0;
 }
 
+/* dK and dV for chosen keys of ONE head (q, k, v, dout are that head's
+ * [N, d] matrices), from the same definition: every query row i that can see
+ * one of the keys (i >= the smallest key under the causal mask, all rows
+ * otherwise) gets its probability row and its dS row once; then
+ * dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i dS_ij Q_i over those rows
+ * (rows that cannot see key j have P_ij = dS_ij = 0).  dk_rows and dv_rows
+ * are [nkeys, d].  Returns 0, or -1 on a bad key or when memory runs out. */
+int oracle_attention_backward_kv_keys(const double *q, const double *k, const double *v,
+                                      const double *dout, long N, long d, double scale,
+                                      int causal, const long *keys, long nkeys,
+                                      double *dk_rows, double *dv_rows)
+{
+    long i0 = causal ? N : 0;
+    for (long r = 0; r < nkeys; ++r) {
+        if (keys[r] < 0 || keys[r] >= N)
+            return -1;
+        if (causal && keys[r] < i0)
+            i0 = keys[r];
+    }
+    if (nkeys == 0)
+        return 0;
+    const long rows = N - i0;
+    double *P = (double *)malloc((size_t)rows * (size_t)N * sizeof(double));
+    double *dS = (double *)malloc((size_t)rows * (size_t)N * sizeof(double));
+    if (!P || !dS) {
+        free(P);
+        free(dS);
+        return -1;
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long i = i0; i < N; ++i) {
+        double *p = P + (i - i0) * N, *ds = dS + (i - i0) * N;
+        score_row(q + i * d, k, i, N, d, scale, causal, ds);
+        oracle_softmax(ds, N, p);
+        grad_score_row(p, dout + i * d, v, N, d, ds);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long r = 0; r < nkeys; ++r) {
+        const long j = keys[r];
+        for (long t = 0; t < d; ++t) {
+            double ak = 0.0, av = 0.0;
+            for (long i = i0; i < N; ++i) {
+                ak += dS[(i - i0) * N + j] * q[i * d + t];
+                av += P[(i - i0) * N + j] * dout[i * d + t];
+            }
+            dk_rows[r * d + t] = scale * ak;
+            dv_rows[r * d + t] = av;
+        }
+    }
+    free(P);
+    free(dS);
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_num_threads(void)
 {

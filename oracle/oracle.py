@@ -82,6 +82,10 @@ class Oracle:
         lib.oracle_attention_backward_dq_rows.restype = ctypes.c_int
         lib.oracle_attention_backward_dq_rows.argtypes = [_D, _D, _D, _D] + [ctypes.c_long] * 4 + [
             ctypes.c_double, ctypes.c_int, _L, ctypes.c_long, _D]
+        lib.oracle_attention_backward_kv_keys.restype = ctypes.c_int
+        lib.oracle_attention_backward_kv_keys.argtypes = [_D, _D, _D, _D, ctypes.c_long,
+                                                          ctypes.c_long, ctypes.c_double,
+                                                          ctypes.c_int, _L, ctypes.c_long, _D, _D]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         self._lib = lib
@@ -170,6 +174,23 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_attention_backward_dq_rows: bad row index or out of memory")
         return out
+
+    def attention_backward_kv_keys(self, q, k, v, dout, scale: float, causal: bool, keys):
+        """One head: q, k, v, dout are [N, d].  Returns (dK rows, dV rows),
+        each [len(keys), d], for the given key indices."""
+        q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+        if not (q.shape == k.shape == v.shape == dout.shape and q.ndim == 2):
+            raise ValueError("q, k, v, dout must share one [N, d] shape")
+        N, d = q.shape
+        kk = np.ascontiguousarray(np.asarray(keys, dtype=np.int64).reshape(-1))
+        dk = np.empty((kk.size, d), dtype=np.float64)
+        dv = np.empty((kk.size, d), dtype=np.float64)
+        rc = self._lib.oracle_attention_backward_kv_keys(
+            _dptr(q), _dptr(k), _dptr(v), _dptr(dout), N, d, float(scale), int(bool(causal)),
+            kk.ctypes.data_as(_L), kk.size, _dptr(dk), _dptr(dv))
+        if rc != 0:
+            raise ValueError("oracle_attention_backward_kv_keys: bad key or out of memory")
+        return dk, dv
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())

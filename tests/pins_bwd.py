@@ -16,7 +16,8 @@ against:
     to the summed output gradient (rows of P sum to 1), the identity
     sum_i <Q_i, dQ_i> = sum_j <K_j, dK_j>, linearity in dO, and equivariance
     under a joint permutation of keys and values;
-  * the rows entry point against the full one.
+  * the entry points for chosen rows (dQ) and chosen keys (dK, dV) against
+    the full one.
 Each ``pin_bwd_*`` takes a loaded ``oracle.Oracle`` and raises AssertionError
 on disagreement.
 """
@@ -167,10 +168,24 @@ def pin_bwd_rows_match_full(o):
         _close(got, dq[rows[:, 0], rows[:, 1], rows[:, 2]], 0.0, f"dQ rows causal={causal}")
 
 
+def pin_bwd_kv_keys_match_full(o):
+    r = _rng(106)
+    N, d = 23, 8
+    q, k, v, dout = (r.normal(0, 1, (1, 1, N, d)) for _ in range(4))
+    for causal in (False, True):
+        _, dk, dv = o.attention_backward(q, k, v, dout, 0.3, causal)
+        for keys in ([0, 7, N - 1], [N - 1], [5, 3, 5]):
+            gk, gv = o.attention_backward_kv_keys(q[0, 0], k[0, 0], v[0, 0], dout[0, 0], 0.3,
+                                                  causal, keys)
+            _close(gk, dk[0, 0, keys], 1e-14, f"dK keys {keys} causal={causal}")
+            _close(gv, dv[0, 0, keys], 1e-14, f"dV keys {keys} causal={causal}")
+
+
 BWD_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_torch_autograd,
     pin_bwd_closed_forms,
     pin_bwd_invariants,
     pin_bwd_rows_match_full,
+    pin_bwd_kv_keys_match_full,
 ]

@@ -96,3 +96,35 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load_library(str(tmp_path / "missing.so"))
+
+
+# fa_bwd: q, k, v, o, dout, lse, dq, dk, dv, delta
+BQ, BK, BV, BO, BD, BL, BDQ, BDK, BDV, BDL = (BASE + i * GAP for i in range(10))
+
+
+def _bwd(**kw):
+    p = dict(q=BQ, k=BK, v=BV, o=BO, dout=BD, lse=BL, dq=BDQ, dk=BDK, dv=BDV, delta=BDL)
+    args = dict(GOOD)
+    for key, val in kw.items():
+        (p if key in p else args)[key] = val
+    return fa.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"], p["dk"],
+                     p["dv"], p["delta"], args["B"], args["H"], args["N"], args["d"],
+                     args["scale"], args["causal"], None)
+
+
+def test_bwd_validation_codes(lib):
+    for name in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta"):
+        assert _bwd(**{name: 0}) == fa.FA_ERR_NULL, name
+    assert _bwd(B=0) == fa.FA_ERR_SHAPE
+    assert _bwd(N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
+    assert _bwd(d=96) == fa.FA_ERR_HEADDIM
+    assert _bwd(scale=float("nan")) == fa.FA_ERR_SCALE
+    assert _bwd(scale=0.0) == fa.FA_ERR_SCALE
+    assert _bwd(dk=BDK + 8) == fa.FA_ERR_ALIGN
+    assert _bwd(delta=BDL + 4) == fa.FA_ERR_ALIGN
+    # every output against every input, and the outputs against each other
+    for out in ("dq", "dk", "dv", "delta"):
+        for src in (BQ, BK, BV, BO, BD, BL):
+            assert _bwd(**{out: src}) == fa.FA_ERR_ALIAS, out
+    assert _bwd(dk=BDQ) == fa.FA_ERR_ALIAS
+    assert _bwd(delta=BDV + 64) == fa.FA_ERR_ALIAS

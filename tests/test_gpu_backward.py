@@ -1,0 +1,175 @@
+"""Parity of the HIP backward pass (fa_bwd, through the C ABI) with the fp64
+oracle's gradients.
+
+Gates, per gradient tensor (dQ, dK, dV), on the same bf16 inputs:
+  ||g_gpu - g_ref||_2 / ||g_ref||_2 <= 1e-2           (over the whole tensor)
+  max |g_gpu - g_ref| <= 2e-2 * max |g_ref|
+Derivation: every product term of a gradient carries at most three bf16
+roundings (P or dS before the product, O inside delta, the stored result),
+each at most 2^-9 relative; independent rounding errors of a sum of many such
+terms add like the terms themselves, so the expected relative L2 error is a
+few 2^-9 ~ 2e-3 (measured 1.8e-3 .. 2.8e-3); the gates leave a margin of
+about 4x.  The largest element error is bounded by the same per-term budget
+relative to the largest gradient magnitude.
+Large logits (Q, K ~ N(0, 4^2)): rows are nearly one-hot, so dP_ij - delta_i
+cancels for the dominant key and the 2^-9 rounding of O inside delta (an
+absolute error of 2^-9 |dO_i||O_i|) becomes a relative error of dS several
+times 2^-9; dQ and dK there measure 6e-3 .. 8e-3 relative L2, and the gates
+for these inputs are doubled (2e-2 relative L2, 4e-2 of the largest
+magnitude).  delta (the workspace output) must equal dO . O_gpu (both bf16,
+widened) to fp32 summation accuracy.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_32_amd as fa
+from exact_attention_32_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 1e-2
+TOL_MAX = 2e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_bwd(q, k, v, dout, causal, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, dout))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa.backward(qd, kd, vd, o, lse, dd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().double().numpy()  # noqa: E731
+    return f64(dq), f64(dk), f64(dv), f64(o), delta.cpu().double().numpy()
+
+
+def check_grad(got, ref, what, big_logits=False):
+    tol_rel, tol_max = (2 * TOL_REL, 2 * TOL_MAX) if big_logits else (TOL_REL, TOL_MAX)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    scale = float(np.abs(ref).max())
+    rel = float(np.linalg.norm((got - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+    mx = float(err.max()) / max(scale, 1e-300)
+    _say(f"  {what}: rel_l2={rel:.3e} max_err/max_ref={mx:.3e} (max_ref={scale:.3e})")
+    assert rel <= tol_rel, f"{what}: rel-L2 {rel}"
+    assert mx <= tol_max, f"{what}: max error {mx} of the largest magnitude"
+
+
+def check_delta(delta, dout, o, what):
+    ref = np.einsum("bhnd,bhnd->bhn", dout.float().double().numpy(), o)
+    bound = 1e-5 * np.einsum("bhnd,bhnd->bhn", np.abs(dout.float().double().numpy()), np.abs(o)) + 1e-30
+    assert np.all(np.abs(delta - ref) <= bound), f"{what}: delta differs from dO . O"
+
+
+SMALL = [
+    # (B, H, N, d, dist, causal)
+    (1, 1, 1, 64, "normal", False),
+    (1, 1, 1, 128, "normal", True),
+    (1, 2, 63, 64, "normal", True),
+    (1, 2, 64, 128, "normal", False),
+    (2, 1, 65, 64, "uniform", True),
+    (1, 3, 127, 128, "normal", True),
+    (1, 2, 128, 64, "normal4", True),
+    (2, 2, 129, 128, "normal", False),
+    (1, 2, 300, 128, "normal4", True),
+    (1, 2, 333, 64, "uniform", False),
+    (1, 2, 1000, 128, "normal", True),
+    (1, 1, 1000, 64, "normal", False),
+    (1, 1, 1100, 128, "uniform", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dist,causal", SMALL)
+def test_bwd_small_shapes(B, H, N, d, dist, causal, oracle_lib):
+    w = inputs.Workload(f"bwd_{B}x{H}x{N}x{d}_{dist}_{int(causal)}", B, H, N, d, "bf16", dist,
+                        causal, seed=2000 + N + d)
+    _say(f"case {w.name}")
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    dq, dk, dv, o, delta = run_bwd(q, k, v, dout, causal, w.scale)
+    rq, rk, rv = oracle_lib.attention_backward(q, k, v, dout, w.scale, causal)
+    big = dist == "normal4"
+    check_grad(dq, rq, w.name + " dQ", big)
+    check_grad(dk, rk, w.name + " dK", big)
+    check_grad(dv, rv, w.name + " dV", big)
+    check_delta(delta, dout, o, w.name)
+
+
+def _sample_keys(w, rng, count):
+    """Keys whose dK/dV the oracle can afford at full size: any key without
+    the mask (all rows see it anyway), the last 96 keys with it (only the
+    last rows see them), plus the first and last key."""
+    if not w.causal:
+        return np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, count)]))
+    lo = max(0, w.N - 96)
+    return np.unique(np.concatenate([[w.N - 1, lo], rng.integers(lo, w.N, count)]))
+
+
+@pytest.mark.parametrize("name", ["w2_bf16_b4h16_n2048_d64", "w3_bf16_b2h32_n8192_d128_causal",
+                                  "w4_bf16_b1h16_n16384_d64_causal_big_logits",
+                                  "w5a_bf16_b16h12_n1000_d64",
+                                  "w5b_bf16_b16h12_n1000_d64_causal"])
+def test_bwd_workloads(name, oracle_lib):
+    """Full-size workloads: sampled dQ rows of every head, sampled dK/dV keys
+    of three heads, computed one by one by the oracle; invariants over every
+    head."""
+    w = inputs.WORKLOADS[name]
+    _say(f"case {w.name} backward (sampled)")
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    dq, dk, dv, o, delta = run_bwd(q, k, v, dout, w.causal, w.scale)
+    rows = inputs.sample_rows(w, 256)
+    rq = oracle_lib.attention_backward_dq_rows(q, k, v, dout, w.scale, w.causal, rows)
+    big = w.dist == "normal4"
+    check_grad(dq[rows[:, 0], rows[:, 1], rows[:, 2]], rq, w.name + " dQ rows", big)
+    rng = np.random.default_rng(w.seed + 77)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))]
+    got_k, got_v, ref_k, ref_v = [], [], [], []
+    for b, h in heads:
+        keys = _sample_keys(w, rng, 12)
+        rk, rv = oracle_lib.attention_backward_kv_keys(q[b, h], k[b, h], v[b, h], dout[b, h],
+                                                       w.scale, w.causal, keys)
+        got_k.append(dk[b, h, keys]); got_v.append(dv[b, h, keys])
+        ref_k.append(rk); ref_v.append(rv)
+    check_grad(np.concatenate(got_k), np.concatenate(ref_k), w.name + " dK keys", big)
+    check_grad(np.concatenate(got_v), np.concatenate(ref_v), w.name + " dV keys", big)
+    # invariants of every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    # (rows of P sum to 1), to the accuracy of the bf16 gradients
+    sk = np.abs(dk.sum(axis=2)).max(axis=-1)
+    nk = np.linalg.norm(dk, axis=(2, 3))
+    assert np.all(sk <= 2e-2 * nk), f"sum_j dK_j not ~0: worst {float((sk / nk).max()):.3e}"
+    dsum = dout.float().double().numpy().sum(axis=2)
+    sv = np.abs(dv.sum(axis=2) - dsum).max(axis=-1)
+    nv = np.linalg.norm(dv, axis=(2, 3))
+    assert np.all(sv <= 2e-2 * nv), f"sum_j dV_j != sum_i dO_i: worst {float((sv / nv).max()):.3e}"
+    check_delta(delta, dout, o, w.name)
+
+
+def test_bwd_deterministic():
+    """No atomics: two runs give bit-identical gradients."""
+    w = inputs.Workload("det", 2, 3, 700, 128, "bf16", "normal", True, seed=5)
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    a = run_bwd(q, k, v, dout, True, w.scale)
+    b = run_bwd(q, k, v, dout, True, w.scale)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_error_codes_on_device():
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    k, v, dout = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    o, lse = fa.forward(q, k, v)
+    with pytest.raises(fa.FAError) as e:
+        fa.backward(q, k, v, o, lse, dout, scale=0.0)
+    assert e.value.code == fa.FA_ERR_SCALE
+    dq = torch.empty_like(q)
+    delta = torch.empty(1, 1, 64, device="cuda")
+    rc = fa.fa_bwd(q, k, v, o, dout, lse, q, dq, dq, delta, 1, 1, 64, 64, 0.125, 0, None)
+    assert rc == fa.FA_ERR_ALIAS
+    rc = fa.fa_bwd(q, k, v, o, dout, lse, dq, torch.empty_like(q), torch.empty_like(q), lse,
+                   1, 1, 64, 64, 0.125, 0, None)
+    assert rc == fa.FA_ERR_ALIAS

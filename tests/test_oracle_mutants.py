@@ -55,6 +55,10 @@ BWD_MUTANTS = {
     "bwd_dv_transposed_p": ("av += P[i * N + j] * doh[i * d + t];", "av += P[j * N + i] * doh[i * d + t];"),
     "bwd_dv_uses_v": ("av += P[i * N + j] * doh[i * d + t];", "av += P[i * N + j] * vh[i * d + t];"),
     "bwd_rows_wrong_index": ("acc += s[j] * kh[j * d + t];", "acc += s[j] * kh[j * d + (t + 1) % d];"),
+    "bwd_keys_first_row_skipped": ("for (long i = i0; i < N; ++i) {\n                ak +=",
+                                   "for (long i = i0 + 1; i < N; ++i) {\n                ak +="),
+    "bwd_keys_dv_uses_ds": ("av += P[(i - i0) * N + j] * dout[i * d + t];",
+                            "av += dS[(i - i0) * N + j] * dout[i * d + t];"),
 }
 
 
