@@ -90,17 +90,19 @@ __device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse
 // Direct-to-LDS copy of one kInner-row tile of a [N, D] bf16 matrix (rows r0
 // .. r0 + kInner - 1; rows >= N read as zeros) into `dst`, swizzled: lane l of
 // load u of wave w writes chunk position q = (u*kWaves + w)*64 + l, and
-// fetches the logical chunk that the swizzle stores there (`src[u]`).
+// fetches the logical chunk that the swizzle stores there.  Load u is 4 KiB
+// (16 or 32 rows) after load 0 on both sides and leaves the row's swizzle
+// term unchanged, so one lane offset `src` (load 0) serves every load.
 template <int D>
 __device__ __forceinline__ void load_tile(const __bf16 *mat, int N, int r0, LDS3 char *dst,
-                                          const uint32_t *src, int wave) {
+                                          uint32_t src, int wave) {
     constexpr int kLoads = kInner * (D / 8) / kThreads;
     const uint32_t bytes = (uint32_t)max(0, min(kInner, N - r0)) * (uint32_t)(D * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat + (size_t)r0 * D, bytes);
 #pragma unroll
     for (int u = 0; u < kLoads; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)(dst + (u * kWaves + wave) * 1024),
-                                                 16, src[u], 0, 0, 0);
+                                                 16, src, u * kWaves * 1024, 0, 0);
 }
 
 // Direct-to-LDS copy of vec[c0 .. c0 + 63] (fp32; entries at or past N read
@@ -112,26 +114,26 @@ __device__ __forceinline__ void load_vec(const float *vec, int N, int c0, LDS3 f
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
 }
 
-// Lane-constant source offsets of load_tile (see there).
+// Lane source offset of load_tile's first load (see there).
 template <int D>
-__device__ __forceinline__ void tile_src_offsets(int wave, int lane, uint32_t *src) {
-    constexpr int kLoads = kInner * (D / 8) / kThreads;
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-        const int q = (u * kWaves + wave) * 64 + lane;
-        const int r = q / (D / 8);
-        const int p = q % (D / 8);
-        src[u] = (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
-    }
+__device__ __forceinline__ uint32_t tile_src_offset(int wave, int lane) {
+    const int q = wave * 64 + lane;
+    const int r = q / (D / 8);
+    const int p = q % (D / 8);
+    return (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
 }
 
-// Byte offsets (within a tile) of the 128-bit operand reads: lane (g, i) reads
-// row i (+32 per 32-row block) and logical chunk 2ks + g.
+// Byte offset (within a tile) of the 128-bit operand read of k-step ks: lane
+// (g, i) reads row i (+32 per 32-row block) and logical chunk 2ks + g.  The
+// stored chunk is (2ks + g) ^ swz(i) = (g ^ swz(i)) ^ 2ks, so the offset is
+// the k-step-0 offset with the chunk field XOR-ed by 32 ks bytes.
 template <int D>
-__device__ __forceinline__ void row_read_offsets(int lane, uint32_t *off) {
+__device__ __forceinline__ uint32_t row_read_offset(int lane) {
     const int g = lane >> 5, i = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) off[ks] = (uint32_t)(i * D * 2 + (((2 * ks + g) ^ swz<D>(i)) << 4));
+    return (uint32_t)(i * D * 2 + ((g ^ swz<D>(i)) << 4));
+}
+__device__ __forceinline__ uint32_t row_read_at(uint32_t base, int ks) {
+    return base ^ (uint32_t)(ks << 5);
 }
 
 // Byte offsets of the transpose reads that form the A operand M^T (M = a
@@ -139,27 +141,27 @@ __device__ __forceinline__ void row_read_offsets(int lane, uint32_t *off) {
 // G = lane/16 (m0 = 16 (G & 1), g = G >> 1), lane i of the group reads the
 // four bf16 of row 16T + 8h + 4g + i/4, columns 32db + m0 + 4(i%4) .. +3; the
 // two halves h = 0, 1 form one 8-element operand.  The swizzle term depends on
-// h (not on T), so each h has its own offsets.
+// h (not on T), so each h has its own offset; d-block db only adds 4db to
+// the logical chunk, i.e. XORs the chunk field with 64 db bytes.
 template <int D>
-__device__ __forceinline__ void tr_read_offsets(int lane, uint32_t (*off)[D / 32]) {
+__device__ __forceinline__ void tr_read_offsets(int lane, uint32_t *off) {
     const int g = lane >> 5, gi = lane & 15, m0 = 16 * ((lane >> 4) & 1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int row = 8 * h + 4 * g + (gi >> 2);
-            const int col = 32 * db + m0 + 4 * (gi & 3);
-            const int c = col >> 3;
-            off[h][db] = (uint32_t)(row * D * 2 + ((c ^ swz<D>(row)) << 4) + ((col & 4) << 1));
-        }
+    for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + 4 * g + (gi >> 2);
+        const int col = m0 + 4 * (gi & 3);
+        const int c = col >> 3;
+        off[h] = (uint32_t)(row * D * 2 + ((c ^ swz<D>(row)) << 4) + ((col & 4) << 1));
+    }
 }
 
 template <int D>
-__device__ __forceinline__ bf16x8 tr_read(const LDS3 char *tile, const uint32_t (*off)[D / 32],
-                                          int T, int db) {
+__device__ __forceinline__ bf16x8 tr_read(const LDS3 char *tile, const uint32_t *off, int T,
+                                          int db) {
     const LDS3 char *base = tile + T * 16 * D * 2;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + off[0][db]));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + off[1][db]));
+    const uint32_t x = (uint32_t)(db << 6);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + (off[0] ^ x)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + (off[1] ^ x)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -187,14 +189,25 @@ __device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, f
 // dq kernel: one workgroup = 128 queries of one (batch, head); wave w owns
 // queries r0 + 32w .. +31 (lane (g, j) holds query j of the wave).
 // ---------------------------------------------------------------------------
+// Both kernels run two waves per SIMD (<= 256 registers per lane).  The
+// dkdv kernel holds K, V and two accumulators in registers (192 of them at
+// d = 128); there its two 32-query halves run as a loop, not unrolled, which
+// keeps their live ranges apart (a few registers still go to scratch, which
+// measured faster than one wave per SIMD).
+template <int D>
+constexpr int kDqWaves = 2;
+template <int D>
+constexpr int kDkdvWaves = 2;
+template <int D>
+constexpr int kHalfUnroll = D == 128 ? 1 : 2;
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>, kDqWaves<D>)))
 bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
               const __bf16 *__restrict__ V, const __bf16 *__restrict__ O,
               const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
               float *__restrict__ Delta, __bf16 *__restrict__ dQ, int N, int ntiles,
               float scale, float scale_log2) {
-    constexpr int kLoads = kInner * (D / 8) / kThreads;
     __shared__ __attribute__((aligned(16))) __bf16 lds_k0[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_k1[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_v0[kInner * D];
@@ -248,11 +261,9 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int kv_end = CAUSAL ? min(N, r0 + kOuter) : N;
     const int n_tiles = (kv_end + kInner - 1) / kInner;
 
-    uint32_t src[kLoads];
-    tile_src_offsets<D>(wave, lane, src);
-    uint32_t rd[D / 16];
-    row_read_offsets<D>(lane, rd);
-    uint32_t trd[2][D / 32];
+    const uint32_t src = tile_src_offset<D>(wave, lane);
+    const uint32_t rd = row_read_offset<D>(lane);
+    uint32_t trd[2];
     tr_read_offsets<D>(lane, trd);
 
     f32x16 acc[D / 32];
@@ -284,8 +295,9 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < kInner / 32; ++kb) {
-                    const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(kt + rd[ks] + kb * 32 * D * 2);
-                    const bf16x8 vf = *reinterpret_cast<const LDS3 bf16x8 *>(vt + rd[ks] + kb * 32 * D * 2);
+                    const uint32_t a = row_read_at(rd, ks) + kb * 32 * D * 2;
+                    const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(kt + a);
+                    const bf16x8 vf = *reinterpret_cast<const LDS3 bf16x8 *>(vt + a);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qop[ks], s[kb], 0, 0, 0);
                     dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, doop[ks], dp[kb], 0, 0, 0);
                 }
@@ -344,13 +356,13 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 // of 64 rows stream through LDS together with their LSE and D values.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>, kDkdvWaves<D>)))
 bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
                 const float *__restrict__ LSE, const float *__restrict__ Delta,
                 __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, int ntiles,
                 float scale, float scale_log2) {
-    constexpr int kLoads = kInner * (D / 8) / kThreads;
     __shared__ __attribute__((aligned(16))) __bf16 lds_q0[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_q1[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_o0[kInner * D];
@@ -397,11 +409,9 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int t_begin = CAUSAL ? k0 / kInner : 0;
     const int n_tiles = (N + kInner - 1) / kInner;
 
-    uint32_t src[kLoads];
-    tile_src_offsets<D>(wave, lane, src);
-    uint32_t rd[D / 16];
-    row_read_offsets<D>(lane, rd);
-    uint32_t trd[2][D / 32];
+    const uint32_t src = tile_src_offset<D>(wave, lane);
+    const uint32_t rd = row_read_offset<D>(lane);
+    uint32_t trd[2];
     tr_read_offsets<D>(lane, trd);
 
     f32x16 acck[D / 32], accv[D / 32];
@@ -432,13 +442,14 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         if (active) {
             // Two halves of 32 queries; element r of a half's block is query
             // c0 + 32qb + 8(r/4) + 4g + r%4 (and the lane's key).
-#pragma unroll
+#pragma unroll kHalfUnroll<D>
             for (int qb = 0; qb < kInner / 32; ++qb) {
                 f32x16 s = {}, dp = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 qf = *reinterpret_cast<const LDS3 bf16x8 *>(qt_ + rd[ks] + qb * 32 * D * 2);
-                    const bf16x8 of = *reinterpret_cast<const LDS3 bf16x8 *>(ot_ + rd[ks] + qb * 32 * D * 2);
+                    const uint32_t a = row_read_at(rd, ks) + qb * 32 * D * 2;
+                    const bf16x8 qf = *reinterpret_cast<const LDS3 bf16x8 *>(qt_ + a);
+                    const bf16x8 of = *reinterpret_cast<const LDS3 bf16x8 *>(ot_ + a);
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kop[ks], s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vop[ks], dp, 0, 0, 0);
                 }
