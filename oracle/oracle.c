@@ -172,6 +172,47 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
 }
 
 /* ---------------------------------------------------------------------------
+ * Queries and keys of different lengths (decode).  The unit-12 causal lesson
+ * notes that a single-token decode step computes only the newest query, which
+ * may attend to every existing key.  Reading used here for Nq queries and Nk
+ * keys (Nq <= Nk): the queries are the LAST Nq positions of the sequence, so
+ * under the causal mask query i (0-based) sits at position Nk - Nq + i and
+ * sees keys j <= Nk - Nq + i; with Nq = Nk this is the top-left mask above,
+ * and with Nq = 1 every key is visible.  Same definition otherwise.
+ * q, o: [B, H, Nq, d]; k, v: [B, H, Nk, d]; lse: [B, H, Nq].
+ * ------------------------------------------------------------------------- */
+int oracle_attention_qk(const double *q, const double *k, const double *v, long B, long H,
+                        long Nq, long Nk, long d, double scale, int causal, double *o,
+                        double *lse)
+{
+    if (Nq < 1 || Nk < Nq)
+        return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)Nk * sizeof(double));
+        double *p = (double *)malloc((size_t)Nk * sizeof(double));
+        if (!s || !p) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long r = 0; r < B * H * Nq; ++r) {
+            if (!s || !p)
+                continue;
+            const long bh = r / Nq, i = r % Nq;
+            /* the mask of score_row with the query at position Nk - Nq + i */
+            score_row(q + r * d, k + bh * Nk * d, Nk - Nq + i, Nk, d, scale, causal, s);
+            lse[r] = oracle_softmax(s, Nk, p);
+            weighted_sum(p, v + bh * Nk * d, Nk, d, o + r * d);
+        }
+        free(s);
+        free(p);
+    }
+    return failed ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Backward pass.  The pages say only that the backward pass recomputes S and P
  * from Q, K and the statistics the forward pass keeps, instead of storing the
  * N x N matrices ("解析 FlashAttention（2）", section 1.2 item (3) and the

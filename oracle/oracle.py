@@ -86,6 +86,9 @@ class Oracle:
         lib.oracle_attention_backward_kv_keys.argtypes = [_D, _D, _D, _D, ctypes.c_long,
                                                           ctypes.c_long, ctypes.c_double,
                                                           ctypes.c_int, _L, ctypes.c_long, _D, _D]
+        lib.oracle_attention_qk.restype = ctypes.c_int
+        lib.oracle_attention_qk.argtypes = [_D, _D, _D] + [ctypes.c_long] * 5 + [
+            ctypes.c_double, ctypes.c_int, _D, _D]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         self._lib = lib
@@ -119,6 +122,25 @@ class Oracle:
             raise MemoryError("oracle_attention: out of memory for S")
         if squeeze:
             return o[0, 0], lse[0, 0]
+        return o, lse
+
+    # -- queries and keys of different lengths (decode) ---------------------
+    def attention_qk(self, q, k, v, scale: float, causal: bool):
+        """q: [B, H, Nq, d]; k, v: [B, H, Nk, d] with Nq <= Nk.  The queries are
+        the last Nq positions (causal: query i sees keys j <= Nk - Nq + i).
+        Returns (O [B, H, Nq, d], LSE [B, H, Nq]) in float64."""
+        q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+        if not (q.ndim == k.ndim == 4 and k.shape == v.shape and q.shape[:2] == k.shape[:2]
+                and q.shape[3] == k.shape[3] and q.shape[2] <= k.shape[2]):
+            raise ValueError("need q [B,H,Nq,d], k and v [B,H,Nk,d], Nq <= Nk")
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
+        o = np.empty_like(q)
+        lse = np.empty((B, H, Nq), dtype=np.float64)
+        rc = self._lib.oracle_attention_qk(_dptr(q), _dptr(k), _dptr(v), B, H, Nq, Nk, d,
+                                           float(scale), int(bool(causal)), _dptr(o), _dptr(lse))
+        if rc != 0:
+            raise ValueError("oracle_attention_qk: bad shape or out of memory")
         return o, lse
 
     # -- selected rows only --------------------------------------------------

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from oracle import oracle as oracle_mod
-from tests import pins, pins_bwd
+from tests import pins, pins_bwd, pins_decode
 
 MUTANTS = {
     "dot_wrong_index": ("dot += q_row[t] * k_row[t];", "dot += q_row[t] * k_row[(t + 1) % d];"),
@@ -62,6 +62,18 @@ BWD_MUTANTS = {
 }
 
 
+# Planted mistakes in the Nq x Nk (decode) entry point; each must fail a decode pin.
+DECODE_MUTANTS = {
+    "qk_top_left_mask": ("score_row(q + r * d, k + bh * Nk * d, Nk - Nq + i, Nk, d, scale, causal, s);",
+                         "score_row(q + r * d, k + bh * Nk * d, i, Nk, d, scale, causal, s);"),
+    "qk_mask_one_late": ("score_row(q + r * d, k + bh * Nk * d, Nk - Nq + i, Nk, d, scale, causal, s);",
+                         "score_row(q + r * d, k + bh * Nk * d, Nk - Nq + i + 1, Nk, d, scale, causal, s);"),
+    "qk_v_wrong_head": ("weighted_sum(p, v + bh * Nk * d, Nk, d, o + r * d);",
+                        "weighted_sum(p, v + (bh ? bh - 1 : 0) * Nk * d, Nk, d, o + r * d);"),
+    "qk_query_index": ("const long bh = r / Nq, i = r % Nq;", "const long bh = r / Nq, i = (r + 1) % Nq;"),
+}
+
+
 def _build_mutant(tmp_path, name, old, new):
     src = open(oracle_mod.SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
@@ -97,3 +109,16 @@ def test_backward_mutant_is_caught(name, tmp_path):
         except (AssertionError, ValueError, FloatingPointError):
             failures.append(pin.__name__)
     assert failures, f"planted mistake {name!r} passed every backward pin"
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_MUTANTS))
+def test_decode_mutant_is_caught(name, tmp_path):
+    old, new = DECODE_MUTANTS[name]
+    o = _build_mutant(tmp_path, name, old, new)
+    failures = []
+    for pin in pins_decode.DECODE_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, FloatingPointError):
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name!r} passed every decode pin"
