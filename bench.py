@@ -9,6 +9,11 @@ the MFMA-peak target is stated for).  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--pass fwd|bwd]
 
+--pass decode times fa_decode (one step = the split kernel and the merge
+kernel) on a decode workload (default: the newest query over B=2, H=32,
+Nk=8192, d=128): HBM-bound, so `value` and `roofline` are GB/s of compulsory
+traffic (read Q, K, V once, write O and LSE) against 8 TB/s.
+
 --pass bwd times the backward pass instead (one step = one fa_bwd call: the
 dq kernel and the dkdv kernel) with the nominal backward FLOPs
 10*B*H*N^2*d (five N x N x d products), halved under the causal mask.
@@ -45,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU * 2.4 GHz * 4096 FLOP/clk
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (used only for fp32 workloads)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_fwd_bf16.hip",
                   "exact_attention_32_amd/csrc/fa_fwd_f32.hip"]
 BWD_KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_bwd_bf16.hip"]
@@ -204,13 +210,98 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     print(f"HBM_BYTES_PER_LAUNCH: {total:.0f}")
 
 
+def bench_decode(args) -> int:
+    import numpy as np
+    import torch
+
+    import exact_attention_32_amd as fa
+    from exact_attention_32_amd import inputs
+
+    w = inputs.DECODE_WORKLOADS[args.workload or inputs.DECODE_HEADLINE]
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_decode_qkv(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    need = fa.fa_decode_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        rc = fa.fa_decode(qd, kd, vd, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, w.causal, 0,
+                          ws, need, stream)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, fa.fa_strerror(rc))
+
+    torch.cuda.synchronize(dev)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            step()
+            b.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    ms_per_step = wall * 1e3 / args.steps
+    gbs = w.bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": "attention decode GB/s on 1 MI355X (bf16, compulsory HBM bytes) + % HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "inputs": w.dist, "pass": "decode",
+                   "bytes_per_step": w.bytes, "flops_per_step": w.flops,
+                   "tflops": round(w.flops / (kernel_ms * 1e-3) / 1e12, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "kernel_ms": round(kernel_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        orc = oracle.default()
+        qn, kn, vn = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            orc.attention_qk(qn, kn, vn, w.scale, w.causal)
+            reps += 1
+            if time.perf_counter() - t0 > min(args.cpu_seconds, 10.0):
+                break
+        dt = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {
+            "value": round(w.bytes / dt / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole workload {reps} time(s), {dt:.2f} s each (fp64 definition "
+                      f"on the same bf16 inputs); bytes = the compulsory bf16 bytes"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -237,6 +328,8 @@ def main() -> int:
     import exact_attention_32_amd as fa
     from exact_attention_32_amd import inputs
 
+    if args.which == "decode":
+        return bench_decode(args)
     name = args.workload or inputs.HEADLINE
     w = inputs.WORKLOADS[name]
     dev = torch.device("cuda:0")

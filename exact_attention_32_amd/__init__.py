@@ -3,9 +3,10 @@
 O = softmax(scale * Q K^T [+ causal mask]) V and the per-row log-sum-exp,
 and the gradients dQ, dK, dV, computed tile by tile in hand-written HIP
 kernels behind the C ABI of ``include/fa.h``.  This package is the thin Python
-binding of that library (``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``,
-``fa_strerror`` with the C names, plus the torch conveniences ``forward`` and
-``backward``) and the seeded input generators in ``inputs``.
+binding of that library (``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``, ``fa_decode``,
+``fa_decode_workspace_size``, ``fa_strerror`` with the C names, plus the torch
+conveniences ``forward``, ``backward`` and ``decode``) and the seeded input
+generators in ``inputs``.
 """
 from ._lib import (  # noqa: F401
     EXPORTS,
@@ -16,11 +17,15 @@ from ._lib import (  # noqa: F401
     FA_ERR_NULL,
     FA_ERR_SCALE,
     FA_ERR_SHAPE,
+    FA_ERR_WORKSPACE,
     FA_OK,
     LIB_PATH,
     FAError,
     backward,
+    decode,
     fa_bwd,
+    fa_decode,
+    fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_f32,
     fa_strerror,

@@ -1,4 +1,4 @@
-"""ctypes binding of libfa (include/fa.h): forward and backward pass.  Argument marshalling only: every
+"""ctypes binding of libfa (include/fa.h): forward, backward and decode.  Argument marshalling only: every
 step of the computation runs in the HIP kernels of the library.
 
 There is no fallback: if ``libfa.so`` has not been built, or cannot be
@@ -21,8 +21,10 @@ FA_ERR_SCALE = 4
 FA_ERR_ALIGN = 5
 FA_ERR_HIP = 6
 FA_ERR_ALIAS = 7
+FA_ERR_WORKSPACE = 8
 
-EXPORTS = ("fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_strerror")
+EXPORTS = ("fa_bwd", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
+           "fa_strerror")
 
 _lib = None
 
@@ -50,6 +52,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_decode.restype = i
+    lib.fa_decode.argtypes = [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t, vp]
+    lib.fa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.fa_decode_workspace_size.argtypes = [i] * 6
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [i]
     _lib = lib
@@ -99,6 +105,21 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal,
                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
                                      int(B), int(H), int(N), int(d), float(scale),
                                      int(bool(causal)), _stream(stream)))
+
+
+def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace,
+              workspace_bytes, stream=None) -> int:
+    """Enqueue the decode kernels; pointers may be ints or tensors.  Returns
+    the fa_status code (0 on success)."""
+    return int(load_library().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
+                                        int(bool(causal)), int(num_splits), _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream)))
+
+
+def fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits=0) -> int:
+    return int(load_library().fa_decode_workspace_size(int(B), int(H), int(Nq), int(Nk),
+                                                       int(d), int(num_splits)))
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -166,3 +187,36 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return dq, dk, dv, delta
+
+
+def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
+           stream=None):
+    """Torch convenience wrapper of fa_decode: q is a contiguous bf16
+    [B, H, Nq, d] device tensor (Nq <= 16), k and v contiguous bf16
+    [B, H, Nk, d].  Allocates O, LSE and the workspace, enqueues the kernels
+    on ``stream`` (default: the current torch stream) and returns (O, LSE)."""
+    import torch
+
+    if not (q.dim() == k.dim() == 4 and k.shape == v.shape and q.shape[:2] == k.shape[:2]
+            and q.shape[3] == k.shape[3]):
+        raise ValueError("need q [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise TypeError("q, k, v must be bfloat16")
+    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits)
+    if need == 0:
+        raise FAError(FA_ERR_SHAPE, fa_strerror(FA_ERR_SHAPE))
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, ws, need, stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return o, lse

@@ -66,6 +66,22 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
     return FA_OK;
 }
 
+bool decode_shape_ok(int B, int H, int Nq, int Nk, int d) {
+    if (B < 1 || H < 1 || Nq < 1 || Nq > fa::kDecodeMaxQueries || Nk < Nq || Nk > (1 << 30))
+        return false;
+    if (d != 64 && d != 128) return false;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    return bh <= ((1ull << 40) - 1) / ((uint64_t)Nk * (uint64_t)d);
+}
+
+// Partial outputs [B,H,S,Nq,d] then partial LSEs [B,H,S,Nq], fp32.
+uint64_t decode_workspace(int B, int H, int Nq, int d, int S, uint64_t *lse_offset) {
+    const uint64_t rows = (uint64_t)B * H * S * Nq;
+    const uint64_t o_bytes = (rows * d * 4 + 255) / 256 * 256;
+    if (lse_offset) *lse_offset = o_bytes;
+    return o_bytes + rows * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +114,46 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
+    if (!decode_shape_ok(B, H, Nq, Nk, d)) return 0;
+    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    return (size_t)decode_workspace(B, H, Nq, d, S, nullptr);
+}
+
+int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int Nq, int Nk, int d, float scale, int causal, int num_splits, void *workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 1 || Nq > fa::kDecodeMaxQueries || Nk < Nq || Nk > (1 << 30))
+        return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    uint64_t lse_off = 0;
+    const uint64_t need = decode_workspace(B, H, Nq, d, S, &lse_off);
+    if (!workspace || (uint64_t)workspace_bytes < need) return FA_ERR_WORKSPACE;
+    for (const void *p : {q, k, v, (const void *)o, (const void *)lse, (const void *)workspace})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    const uint64_t q_bytes = bh * Nq * d * 2, kv_bytes = bh * (uint64_t)Nk * d * 2;
+    const uint64_t l_bytes = bh * Nq * 4;
+    struct Span { const void *p; uint64_t n; };
+    const Span ins[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
+    const Span outs[] = {{o, q_bytes}, {lse, l_bytes}, {workspace, need}};
+    for (const Span &w : outs)
+        for (const Span &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_ALIAS;
+    for (int a = 0; a < 3; ++a)
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return FA_ERR_ALIAS;
+    float *o_part = static_cast<float *>(workspace);
+    float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
+    const hipError_t e = fa::launch_decode_bf16(q, k, v, o, lse, B, H, Nq, Nk, d, scale,
+                                                causal != 0, S, o_part, lse_part, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char *fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";
@@ -108,6 +164,7 @@ const char *fa_strerror(int status) {
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
         case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";
         case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL or smaller than required";
         default: return "unknown fa status code";
     }
 }

@@ -1,0 +1,312 @@
+// fa_decode_bf16.hip -- attention of a few queries over many keys (decode)
+// for gfx950: bf16 Q, K, V, O; fp32 scores, softmax statistics and sums.
+//
+// What is computed: O = softmax(scale * Q K^T [+ mask]) V and the per-row
+// log-sum-exp for Nq <= 16 queries over Nk keys of each (batch, head), the
+// queries being the last Nq positions (under the mask query i sees keys
+// j <= Nk - Nq + i; a single query sees every key, as the unit-12 causal
+// lesson says of a single-token decode step).
+//
+// Split of the key axis (the unit-12 loop-order lesson names split-K among
+// the schedules real kernels use): the Nk keys of a head are cut into S
+// chunks, one single-wave workgroup per (batch, head, chunk).  Each workgroup
+// produces the normalised partial output O_s and LSE_s of its chunk; a second
+// kernel merges the chunks with the two-block rule of "解析 FlashAttention（2）"
+// (eq. (17)/(20) for the statistics, (37) for the output):
+//   LSE = ln sum_s e^(LSE_s),   O = sum_s e^(LSE_s - LSE) O_s.
+//
+// With a handful of queries the work is a matrix-vector product: about Nq
+// FLOP per byte of K and V, far below the MFMA balance point, so the kernel
+// is bound by HBM and runs on the vector ALUs.  Layout of a wave: groups of
+// G = d/8 lanes each hold one key row (16 bytes per lane), so one load
+// instruction reads 64/G consecutive rows (1 KiB, coalesced); the dot product
+// of a row with each query is summed over its group with DPP lane moves; every
+// group runs its own online softmax (running max m, sum l, unnormalised
+// output) over the rows it reads, and the groups are merged with the same
+// two-block rule at the end.  K and V rows go straight from HBM into
+// registers (each row is used by one wave only, so LDS would add nothing).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float dpp_add(float x, int ctrl_sel) {
+    // ctrl values: quad_perm [1,0,3,2] = 0xb1, quad_perm [2,3,0,1] = 0x4e,
+    // row_half_mirror = 0x141, row_mirror = 0x140.
+    int y;
+    switch (ctrl_sel) {
+        case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false); break;
+        case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false); break;
+        case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false); break;
+        default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false); break;
+    }
+    return x + __int_as_float(y);
+}
+
+// Sum over the G lanes of a group (G = 8: half a DPP row; G = 16: a row);
+// every lane of the group receives the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    x = dpp_add(x, 0);
+    x = dpp_add(x, 1);
+    x = dpp_add(x, 2);
+    if (G == 16) x = dpp_add(x, 3);
+    return x;
+}
+
+// Merge the online-softmax state (m, l, acc) of another stream into this one
+// (two-block rule; m in raw score units, exponentials in base 2 with `c` =
+// scale * log2(e)).  A stream that has seen no visible key has m = -inf.
+template <int E>
+__device__ __forceinline__ void merge_state(float &m, float &l, float *acc, float mo, float lo,
+                                            const float *ao, float c) {
+    const float mn = fmaxf(m, mo);
+    if (mn == -INFINITY) return;
+    const float a = __builtin_amdgcn_exp2f((m - mn) * c);   // 0 when m = -inf
+    const float b = __builtin_amdgcn_exp2f((mo - mn) * c);
+    l = l * a + lo * b;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * a + ao[e] * b;
+    m = mn;
+}
+
+// One workgroup (one wave) = one (batch*head, key chunk).  Writes the
+// chunk's normalised partial output and LSE (0 and -inf for a query that
+// sees no key of the chunk).
+template <int D, int NQ, bool CAUSAL>
+__global__ void __launch_bounds__(64)
+decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
+                    const __bf16 *__restrict__ V, float *__restrict__ o_part,
+                    float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
+                    float scale_log2) {
+    constexpr int G = D / 8;       // lanes per key row
+    constexpr int RPW = 64 / G;    // rows per load instruction
+    constexpr int ROUNDS = NQ <= 2 ? 8 : (NQ <= 4 ? 4 : 2);
+    constexpr int BLK = RPW * ROUNDS;  // keys per block of loads
+
+    const int lane = threadIdx.x;
+    const int grp = lane / G;
+    const int col = lane % G;
+    const int s = blockIdx.x % S;
+    const int bh = blockIdx.x / S;
+    const int k0 = s * chunk;
+    const int k1 = min(Nk, k0 + chunk);
+
+    // This lane's 8 columns of every query, widened to fp32.
+    float qf[NQ][8];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (qi < Nq) w = *reinterpret_cast<const u32x4 *>(Q + ((size_t)bh * Nq + qi) * D + col * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qf[qi][2 * e] = bf16_lo(w[e]);
+            qf[qi][2 * e + 1] = bf16_hi(w[e]);
+        }
+    }
+    float m[NQ], l[NQ], acc[NQ][8];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+        m[qi] = -INFINITY;
+        l[qi] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
+    }
+
+    const __bf16 *Kh = K + (size_t)bh * Nk * D + col * 8;
+    const __bf16 *Vh = V + (size_t)bh * Nk * D + col * 8;
+    for (int base = k0; base < k1; base += BLK) {
+        u32x4 kr[ROUNDS], vr[ROUNDS];
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const int j = base + r * RPW + grp;
+            kr[r] = vr[r] = u32x4{0u, 0u, 0u, 0u};
+            if (j < k1) {
+                kr[r] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)j * D);
+                vr[r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)j * D);
+            }
+        }
+        // Scores of the block's rows (identical in all G lanes of a group).
+        float sc[ROUNDS][NQ];
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const int j = base + r * RPW + grp;
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                float x = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x = __builtin_fmaf(qf[qi][2 * e], bf16_lo(kr[r][e]), x);
+                    x = __builtin_fmaf(qf[qi][2 * e + 1], bf16_hi(kr[r][e]), x);
+                }
+                x = group_sum<G>(x);
+                const bool hidden = j >= k1 || (CAUSAL && j > Nk - Nq + qi);
+                sc[r][qi] = hidden ? -INFINITY : x;
+            }
+        }
+        // Online softmax of this group's stream, one update per block.
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            float mb = sc[0][qi];
+#pragma unroll
+            for (int r = 1; r < ROUNDS; ++r) mb = fmaxf(mb, sc[r][qi]);
+            const float mn = fmaxf(m[qi], mb);
+            if (mn == -INFINITY) continue;  // nothing visible yet
+            const float alpha = __builtin_amdgcn_exp2f((m[qi] - mn) * scale_log2);
+            const float mc = mn * scale_log2;
+            float ps = 0.f, add[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) add[e] = 0.f;
+#pragma unroll
+            for (int r = 0; r < ROUNDS; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][qi], scale_log2, -mc));
+                ps += p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    add[2 * e] = __builtin_fmaf(p, bf16_lo(vr[r][e]), add[2 * e]);
+                    add[2 * e + 1] = __builtin_fmaf(p, bf16_hi(vr[r][e]), add[2 * e + 1]);
+                }
+            }
+            l[qi] = l[qi] * alpha + ps;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[qi][e] = acc[qi][e] * alpha + add[e];
+            m[qi] = mn;
+        }
+    }
+
+    // Merge the RPW group streams of the wave (lanes G, 2G, ... apart).
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1) {
+            const float mo = __shfl_xor(m[qi], off);
+            const float lo = __shfl_xor(l[qi], off);
+            float ao[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ao[e] = __shfl_xor(acc[qi][e], off);
+            merge_state<8>(m[qi], l[qi], acc[qi], mo, lo, ao, scale_log2);
+        }
+    }
+
+    if (grp == 0) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (qi >= Nq) break;
+            const size_t prow = ((size_t)bh * S + s) * Nq + qi;
+            const float inv = l[qi] > 0.f ? 1.f / l[qi] : 0.f;
+            float *dst = o_part + prow * D + col * 8;
+#pragma unroll
+            for (int e = 0; e < 8; e += 4)
+                *reinterpret_cast<float4 *>(dst + e) =
+                    make_float4(acc[qi][e] * inv, acc[qi][e + 1] * inv, acc[qi][e + 2] * inv,
+                                acc[qi][e + 3] * inv);
+            if (col == 0) lse_part[prow] = l[qi] > 0.f ? m[qi] * scale + logf(l[qi]) : -INFINITY;
+        }
+    }
+}
+
+// One workgroup of D threads per output row (batch*head, query): merges the
+// S partial rows.  Every query sees key 0, so some chunk has a finite LSE.
+template <int D>
+__global__ void __launch_bounds__(D)
+decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ lse_part,
+                    __bf16 *__restrict__ O, float *__restrict__ LSE, int Nq, int S) {
+    const int row = blockIdx.x;  // bh * Nq + qi
+    const int bh = row / Nq, qi = row - bh * Nq;
+    const int t = threadIdx.x;
+    const float *lp = lse_part + (size_t)bh * S * Nq + qi;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(size_t)s * Nq]);
+    float sum = 0.f;
+    for (int s = 0; s < S; ++s) sum += __builtin_amdgcn_exp2f((lp[(size_t)s * Nq] - mx) * kLog2e);
+    const float lse = mx + logf(sum);
+    float acc = 0.f;
+    const float *op = o_part + ((size_t)bh * S * Nq + qi) * D + t;
+    for (int s = 0; s < S; ++s) {
+        const float w = __builtin_amdgcn_exp2f((lp[(size_t)s * Nq] - lse) * kLog2e);
+        if (w > 0.f) acc = __builtin_fmaf(w, op[(size_t)s * Nq * D], acc);
+    }
+    O[(size_t)row * D + t] = (__bf16)acc;
+    if (t == 0) LSE[row] = lse;
+}
+
+template <int D, int NQ, bool CAUSAL>
+hipError_t launch_nq(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int H, int Nq, int Nk, int S, int chunk, float scale, float *o_part,
+                     float *lse_part, hipStream_t stream) {
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipLaunchKernelGGL((decode_split_kernel<D, NQ, CAUSAL>), dim3(B * H * S), dim3(64), 0, stream,
+                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
+                       static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk, scale,
+                       scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(B * H * Nq), dim3(D), 0, stream, o_part,
+                       lse_part, static_cast<__bf16 *>(o), lse, Nq, S);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_d(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                    int Nq, int Nk, int S, int chunk, float scale, float *o_part, float *lse_part,
+                    hipStream_t stream) {
+#define FA_DECODE_NQ(NQ)                                                                      \
+    return launch_nq<D, NQ, CAUSAL>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,  \
+                                    lse_part, stream)
+    if (Nq <= 1) FA_DECODE_NQ(1);
+    if (Nq <= 2) FA_DECODE_NQ(2);
+    if (Nq <= 4) FA_DECODE_NQ(4);
+    if (Nq <= 8) FA_DECODE_NQ(8);
+    FA_DECODE_NQ(16);
+#undef FA_DECODE_NQ
+}
+
+}  // namespace
+
+int decode_num_splits(int B, int H, int Nk, int requested) {
+    if (requested > 0) return min(requested, (Nk + kDecodeMinChunk - 1) / kDecodeMinChunk);
+    // About kDecodeTargetWaves single-wave workgroups in all, chunks of at
+    // least kDecodeMinChunk keys.
+    const long bh = (long)B * H;
+    long s = (kDecodeTargetWaves + bh - 1) / bh;
+    const long smax = (Nk + kDecodeMinChunk - 1) / kDecodeMinChunk;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+int decode_chunk(int Nk, int S) {
+    // a multiple of 64 keys (whole blocks of loads at both head dims)
+    const int c = (Nk + S - 1) / S;
+    return (c + 63) / 64 * 64;
+}
+
+hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                              int S, float *o_part, float *lse_part, hipStream_t stream) {
+    const int chunk = decode_chunk(Nk, S);
+    S = (Nk + chunk - 1) / chunk;  // no empty chunk
+    if (d == 64)
+        return causal ? launch_d<64, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
+                                           lse_part, stream)
+                      : launch_d<64, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
+                                            lse_part, stream);
+    return causal ? launch_d<128, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
+                                        lse_part, stream)
+                  : launch_d<128, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
+                                         lse_part, stream);
+}
+
+}  // namespace fa

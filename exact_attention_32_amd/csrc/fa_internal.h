@@ -23,4 +23,18 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            float *delta, int B, int H, int N, int d, float scale, bool causal,
                            hipStream_t stream);
 
+// Decode (few queries over many keys, key axis split in chunks).
+constexpr int kDecodeMaxQueries = 16;
+constexpr int kDecodeMinChunk = 64;       // keys per chunk, at least
+constexpr int kDecodeTargetWaves = 2048;  // single-wave workgroups aimed for
+// Number of chunks for a requested count (<= 0: automatic).
+int decode_num_splits(int B, int H, int Nk, int requested);
+// Keys per chunk for S chunks (a multiple of 64).
+int decode_chunk(int Nk, int S);
+// Enqueues the split kernel (partials into o_part [B,H,S,Nq,d] and lse_part
+// [B,H,S,Nq], fp32) and the merge kernel.
+hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                              int S, float *o_part, float *lse_part, hipStream_t stream);
+
 }  // namespace fa

@@ -98,6 +98,71 @@ def make_qkv(w: Workload, device="cpu"):
     return tuple(t.to(dt).contiguous().to(device) for t in (q, k, v))
 
 
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq queries (the newest positions) over Nk keys of each (batch, head)."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dist: str
+    causal: bool
+    seed: int
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def flops(self) -> float:
+        """Matmul FLOPs 4*d per visible (query, key) pair."""
+        if self.causal:
+            pairs = sum(self.Nk - self.Nq + i + 1 for i in range(self.Nq))
+        else:
+            pairs = self.Nq * self.Nk
+        return 4.0 * self.B * self.H * pairs * self.d
+
+    @property
+    def bytes(self) -> float:
+        """Compulsory HBM bytes: read Q, K, V once, write O (bf16) and LSE."""
+        bh = self.B * self.H
+        return 2.0 * bh * (2 * self.Nk + 2 * self.Nq) * self.d + 4.0 * bh * self.Nq
+
+
+# Decode steps over the key/value shapes of the workloads above: the newest
+# query (or 16 of them, masked) of each sequence.
+DECODE_WORKLOADS = {
+    "d3_bf16_b2h32_nq1_nk8192_d128": DecodeWorkload("d3_bf16_b2h32_nq1_nk8192_d128", 2, 32, 1, 8192, 128, "normal", False, 13),
+    "d3q16_bf16_b2h32_nq16_nk8192_d128_causal": DecodeWorkload("d3q16_bf16_b2h32_nq16_nk8192_d128_causal", 2, 32, 16, 8192, 128, "normal", True, 23),
+    "d4_bf16_b1h16_nq1_nk16384_d64_big_logits": DecodeWorkload("d4_bf16_b1h16_nq1_nk16384_d64_big_logits", 1, 16, 1, 16384, 64, "normal4", False, 14),
+    "d5_bf16_b16h12_nq1_nk1000_d64": DecodeWorkload("d5_bf16_b16h12_nq1_nk1000_d64", 16, 12, 1, 1000, 64, "uniform", False, 15),
+}
+
+DECODE_HEADLINE = "d3_bf16_b2h32_nq1_nk8192_d128"
+
+
+def make_decode_qkv(w: DecodeWorkload, device="cpu"):
+    """(q [B,H,Nq,d], k, v [B,H,Nk,d]) with the recipe of make_qkv (Q, then K,
+    then V from one generator seeded with the workload's seed)."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+
+    def draw(shape, big):
+        if w.dist == "uniform":
+            return 2.0 * torch.rand(shape, generator=g, dtype=torch.float32) - 1.0
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        return 4.0 * x if big else x
+
+    big = w.dist == "normal4"
+    q = draw((w.B, w.H, w.Nq, w.d), big)
+    k = draw((w.B, w.H, w.Nk, w.d), big)
+    v = draw((w.B, w.H, w.Nk, w.d), False)
+    dt = torch_dtype(w.dtype)
+    return tuple(t.to(dt).contiguous().to(device) for t in (q, k, v))
+
+
 def make_dout(w: Workload, device="cpu"):
     """The output gradient dO for the backward pass: i.i.d. N(0, 1) from a
     generator seeded with seed + 10000, as fp32 [B, H, N, d] rounded to the

@@ -60,7 +60,8 @@ enum fa_status {
     FA_ERR_SCALE = 4,    /* scale is not finite, or not > 0                  */
     FA_ERR_ALIGN = 5,    /* a pointer is not 16-byte aligned                 */
     FA_ERR_HIP = 6,      /* the kernel launch failed (hipGetLastError)       */
-    FA_ERR_ALIAS = 7     /* an output overlaps an input or another output    */
+    FA_ERR_ALIAS = 7,    /* an output overlaps an input or another output    */
+    FA_ERR_WORKSPACE = 8 /* workspace NULL or smaller than required          */
 };
 
 /*
@@ -119,6 +120,44 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            const float *lse, void *dq, void *dk, void *dv, float *delta,
            int B, int H, int N, int d, float scale, int causal,
            hipStream_t stream);
+
+/*
+ * fa_decode -- attention of a few queries over many keys (a decode step):
+ * O = softmax(scale * Q K^T [+ mask]) V with its LSE, for Nq <= 16 queries
+ * per (batch, head) over Nk >= Nq keys.
+ *
+ * The queries are the LAST Nq positions of the sequence.  With causal != 0,
+ * query i (0-based) sits at position Nk - Nq + i and sees keys
+ * j <= Nk - Nq + i (for Nq = Nk this is fa_fwd's mask; a single query sees
+ * every key, as the unit-12 causal lesson of "在线 Softmax 与 FlashAttention"
+ * says of a single-token decode step).  The key axis is split into chunks
+ * processed in parallel (split-K, named in that course's loop-order lesson);
+ * each chunk's partial output and LSE are merged with the two-block rule of
+ * "解析 FlashAttention（2）", eq. (17)/(20) and (37):
+ *   LSE = ln sum_s e^(LSE_s),   O = sum_s e^(LSE_s - LSE) O_s.
+ *
+ *   q         : const bf16 [B, H, Nq, d]
+ *   k, v      : const bf16 [B, H, Nk, d]
+ *   o         : bf16 [B, H, Nq, d], written (rounded to nearest even)
+ *   lse       : fp32 [B, H, Nq], written (natural log, as fa_fwd)
+ *   num_splits: chunks of the key axis; <= 0 chooses automatically (about
+ *               2048 chunks over all heads, at least 64 keys each); a larger
+ *               request is cut to ceil(Nk / 64)
+ *   workspace : device memory of at least fa_decode_workspace_size(...)
+ *               bytes for the fp32 partials; its contents on return are
+ *               unspecified; it must not overlap any other argument
+ * Scores, statistics and sums are fp32.  Shapes: B, H >= 1, 1 <= Nq <= 16,
+ * Nq <= Nk <= 2^30, d is 64 or 128, B*H*Nk*d < 2^40.  Two kernels are enqueued
+ * on `stream`.  Errors as for fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              int num_splits, void *workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/* Bytes of workspace fa_decode needs for these arguments (0 if they are
+ * invalid shapes). */
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_strerror(int status);

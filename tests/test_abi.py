@@ -39,11 +39,11 @@ def test_status_codes_match_header():
 
 
 def test_strerror(lib):
-    for code in range(8):
+    for code in range(9):
         s = fa.fa_strerror(code)
         assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM",
                              "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP",
-                             "FA_ERR_ALIAS"][code])
+                             "FA_ERR_ALIAS", "FA_ERR_WORKSPACE"][code])
     assert "unknown" in fa.fa_strerror(99)
     assert "unknown" in fa.fa_strerror(-1)
 
@@ -128,3 +128,36 @@ def test_bwd_validation_codes(lib):
             assert _bwd(**{out: src}) == fa.FA_ERR_ALIAS, out
     assert _bwd(dk=BDQ) == fa.FA_ERR_ALIAS
     assert _bwd(delta=BDV + 64) == fa.FA_ERR_ALIAS
+
+
+def test_decode_workspace_size(lib):
+    ws = fa.fa_decode_workspace_size
+    assert ws(1, 1, 1, 100, 64, 0) > 0
+    assert ws(2, 32, 1, 8192, 128, 0) >= 2 * 32 * 1 * 129 * 4   # at least one chunk
+    assert ws(1, 1, 1, 100, 64, 1) < ws(1, 1, 1, 100, 64, 2)
+    assert ws(1, 1, 1, 4096, 128, 10 ** 6) == ws(1, 1, 1, 4096, 128, 64)   # capped at Nk/64
+    for bad in ((0, 1, 1, 100, 64, 0), (1, 1, 0, 100, 64, 0), (1, 1, 17, 100, 64, 0),
+                (1, 1, 8, 7, 64, 0), (1, 1, 1, 100, 96, 0)):
+        assert ws(*bad) == 0, bad
+
+
+def test_decode_validation_codes(lib):
+    DQ, DK, DV, DO, DL, DW = (BASE + i * GAP for i in range(6))
+
+    def call(q=DQ, k=DK, v=DV, o=DO, lse=DL, ws=DW, B=2, H=3, Nq=1, Nk=500, d=128,
+             scale=0.125, causal=0, splits=0, wsb=1 << 30):
+        return fa.fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, splits, ws, wsb,
+                            None)
+    assert call(q=0) == fa.FA_ERR_NULL
+    assert call(lse=0) == fa.FA_ERR_NULL
+    assert call(Nq=0) == fa.FA_ERR_SHAPE
+    assert call(Nq=17) == fa.FA_ERR_SHAPE
+    assert call(Nq=8, Nk=7) == fa.FA_ERR_SHAPE
+    assert call(d=80) == fa.FA_ERR_HEADDIM
+    assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(ws=0) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=16) == fa.FA_ERR_WORKSPACE
+    assert call(o=DO + 8) == fa.FA_ERR_ALIGN
+    assert call(ws=DK) == fa.FA_ERR_ALIAS
+    assert call(o=DQ) == fa.FA_ERR_ALIAS
+    assert call(lse=DW + 64) == fa.FA_ERR_ALIAS
