@@ -217,29 +217,89 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     }
 }
 
-// One workgroup of D threads per output row (batch*head, query): merges the
-// S partial rows.  Every query sees key 0, so some chunk has a finite LSE.
+// Merge kernel: one workgroup of 256 threads per output row (batch*head,
+// query) combines the row's S partial rows.  Every query sees key 0, so some
+// chunk has a finite LSE.
+//  1. LSE = ln sum_s e^(LSE_s): each thread folds its share of the S values
+//     into a (max, sum) pair; the pairs are merged across the workgroup.
+//  2. O = sum_s e^(LSE_s - LSE) O_s: the weights of up to kMergeChunk chunks
+//     at a time go to LDS; thread t adds column t % D of the chunks
+//     s = t / D (mod 256 / D), with independent loads; the 256 / D slices
+//     are summed through LDS at the end.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 1024;
+
+__device__ __forceinline__ void fold_lse(float &m, float &l, float x) {
+    if (x == -INFINITY) return;
+    if (x > m) {
+        l = l * __builtin_amdgcn_exp2f((m - x) * kLog2e) + 1.f;
+        m = x;
+    } else {
+        l += __builtin_amdgcn_exp2f((x - m) * kLog2e);
+    }
+}
+
+__device__ __forceinline__ void merge_pair(float &m, float &l, float mo, float lo) {
+    const float mn = fmaxf(m, mo);
+    if (mn == -INFINITY) return;
+    l = l * __builtin_amdgcn_exp2f((m - mn) * kLog2e) + lo * __builtin_amdgcn_exp2f((mo - mn) * kLog2e);
+    m = mn;
+}
+
 template <int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ lse_part,
                     __bf16 *__restrict__ O, float *__restrict__ LSE, int Nq, int S) {
+    constexpr int kSlices = kMergeThreads / D;
+    __shared__ float wts[kMergeChunk];
+    __shared__ float red_m[kMergeThreads / 64], red_l[kMergeThreads / 64];
+    __shared__ float part[kMergeThreads];
     const int row = blockIdx.x;  // bh * Nq + qi
     const int bh = row / Nq, qi = row - bh * Nq;
     const int t = threadIdx.x;
     const float *lp = lse_part + (size_t)bh * S * Nq + qi;
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(size_t)s * Nq]);
-    float sum = 0.f;
-    for (int s = 0; s < S; ++s) sum += __builtin_amdgcn_exp2f((lp[(size_t)s * Nq] - mx) * kLog2e);
-    const float lse = mx + logf(sum);
-    float acc = 0.f;
-    const float *op = o_part + ((size_t)bh * S * Nq + qi) * D + t;
-    for (int s = 0; s < S; ++s) {
-        const float w = __builtin_amdgcn_exp2f((lp[(size_t)s * Nq] - lse) * kLog2e);
-        if (w > 0.f) acc = __builtin_fmaf(w, op[(size_t)s * Nq * D], acc);
+
+    float m = -INFINITY, l = 0.f;
+    for (int s = t; s < S; s += kMergeThreads) fold_lse(m, l, lp[(size_t)s * Nq]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) merge_pair(m, l, __shfl_xor(m, off), __shfl_xor(l, off));
+    if ((t & 63) == 0) {
+        red_m[t >> 6] = m;
+        red_l[t >> 6] = l;
     }
-    O[(size_t)row * D + t] = (__bf16)acc;
-    if (t == 0) LSE[row] = lse;
+    __syncthreads();
+    m = red_m[0];
+    l = red_l[0];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / 64; ++w) merge_pair(m, l, red_m[w], red_l[w]);
+    const float lse = m + logf(l);
+
+    const int c = t % D, slice = t / D;
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
+        const int n = min(kMergeChunk, S - s0);
+        __syncthreads();  // the previous chunk's weights are no longer read
+        for (int s = t; s < n; s += kMergeThreads)
+            wts[s] = __builtin_amdgcn_exp2f((lp[(size_t)(s0 + s) * Nq] - lse) * kLog2e);
+        __syncthreads();
+        const float *op = o_part + (((size_t)bh * S + s0) * Nq + qi) * D + c;
+        const size_t stride = (size_t)Nq * D;
+        int s = slice;
+        for (; s + kSlices < n; s += 2 * kSlices) {
+            acc0 = __builtin_fmaf(wts[s], op[(size_t)s * stride], acc0);
+            acc1 = __builtin_fmaf(wts[s + kSlices], op[(size_t)(s + kSlices) * stride], acc1);
+        }
+        if (s < n) acc0 = __builtin_fmaf(wts[s], op[(size_t)s * stride], acc0);
+    }
+    part[t] = acc0 + acc1;
+    __syncthreads();
+    if (slice == 0) {
+        float o = part[c];
+#pragma unroll
+        for (int k = 1; k < kSlices; ++k) o += part[k * D + c];
+        O[(size_t)row * D + c] = (__bf16)o;
+        if (c == 0) LSE[row] = lse;
+    }
 }
 
 template <int D, int NQ, bool CAUSAL>
@@ -253,8 +313,8 @@ hipError_t launch_nq(const void *q, const void *k, const void *v, void *o, float
                        scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(B * H * Nq), dim3(D), 0, stream, o_part,
-                       lse_part, static_cast<__bf16 *>(o), lse, Nq, S);
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(B * H * Nq), dim3(kMergeThreads), 0, stream,
+                       o_part, lse_part, static_cast<__bf16 *>(o), lse, Nq, S);
     return hipGetLastError();
 }
 
