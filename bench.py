@@ -14,6 +14,13 @@ kernel) on a decode workload (default: the newest query over B=2, H=32,
 Nk=8192, d=128): HBM-bound, so `value` and `roofline` are GB/s of compulsory
 traffic (read Q, K, V once, write O and LSE) against 8 TB/s.
 
+--pass kvouter times fa_fwd_kv_outer (the forward pass in Algorithm 1's
+key/value-outer order, one launch per 64-key block, O, l, m round-tripping
+through device memory) on a forward workload: same FLOPs and metric as the
+forward pass; its roofline is HBM, with the algorithm's own traffic per call
+(each step reads Q_i and the O_i, l_i, m_i state and writes the state back;
+K_j, V_j once per step and head) counted from the block geometry.
+
 --pass bwd times the backward pass instead (one step = one fa_bwd call: the
 dq kernel and the dkdv kernel) with the nominal backward FLOPs
 10*B*H*N^2*d (five N x N x d products), halved under the causal mask.
@@ -210,6 +217,33 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     print(f"HBM_BYTES_PER_LAUNCH: {total:.0f}")
 
 
+def kvouter_bytes(w) -> float:
+    """HBM bytes the key/value-outer order moves per call, counted per
+    (query block i, key block j) step as Algorithm 1 states them: read Q_i
+    and (after the first step) O_i, l_i, m_i; write O_i, l_i, m_i (fp32), or
+    at a row block's last step the bf16 O_i and its LSE; K_j and V_j once per
+    key block and head."""
+    Br, Bc = 128, 64
+    nqb, nkb = -(-w.N // Br), -(-w.N // Bc)
+    total = 0.0
+    for j in range(nkb):
+        rows_j = min(Bc, w.N - j * Bc)
+        total += 2 * rows_j * w.d * 2
+        i0 = (j * Bc) // Br if w.causal else 0
+        for i in range(i0, nqb):
+            rows = min(Br, w.N - i * Br)
+            last_row = min(w.N, (i + 1) * Br) - 1
+            j_last = last_row // Bc if w.causal else nkb - 1
+            total += rows * w.d * 2                      # Q_i
+            if j > 0:
+                total += rows * (w.d * 4 + 8)            # O_i, l_i, m_i read
+            if j == j_last:
+                total += rows * (w.d * 2 + 4)            # bf16 O_i and LSE
+            else:
+                total += rows * (w.d * 4 + 8)            # O_i, l_i, m_i written
+    return total * w.B * w.H
+
+
 def bench_decode(args) -> int:
     import numpy as np
     import torch
@@ -301,7 +335,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode", "kvouter"),
+                    default="fwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -345,6 +380,18 @@ def main() -> int:
         rc = fn(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, stream)
         if rc != fa.FA_OK:
             raise fa.FAError(rc, fa.fa_strerror(rc))
+
+    if args.which == "kvouter":
+        if w.dtype != "bf16":
+            raise SystemExit("the key/value-outer pass is bf16 only")
+        kv_need = fa.fa_fwd_kv_outer_workspace_size(w.B, w.H, w.N, w.d)
+        kv_ws = torch.empty(kv_need, dtype=torch.uint8, device=dev)
+
+        def step():  # noqa: F811
+            rc = fa.fa_fwd_kv_outer(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal,
+                                    kv_ws, kv_need, stream)
+            if rc != fa.FA_OK:
+                raise fa.FAError(rc, fa.fa_strerror(rc))
 
     if args.which == "bwd":
         if w.dtype != "bf16":
@@ -398,6 +445,16 @@ def main() -> int:
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     metric = "attention fwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": read_traffic(w.name) if args.which == "fwd" else None,
+                "kernel_ms": round(kernel_ms, 4)}
+    if args.which == "kvouter":
+        nbytes = kvouter_bytes(w)
+        gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": nbytes}
     if args.which == "bwd":
         metric = "attention bwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
     line = {
@@ -417,10 +474,7 @@ def main() -> int:
                    "causal": w.causal, "inputs": w.dist, "pass": args.which,
                    "flops_per_step": flops,
                    "pct_mfma_peak": round(100 * tflops / peak, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": read_traffic(w.name) if args.which == "fwd" else None,
-                     "kernel_ms": round(kernel_ms, 4)},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         if args.which == "bwd":

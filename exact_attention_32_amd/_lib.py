@@ -24,7 +24,7 @@ FA_ERR_ALIAS = 7
 FA_ERR_WORKSPACE = 8
 
 EXPORTS = ("fa_bwd", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
-           "fa_strerror")
+           "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size", "fa_strerror")
 
 _lib = None
 
@@ -56,6 +56,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode.argtypes = [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t, vp]
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_decode_workspace_size.argtypes = [i] * 6
+    lib.fa_fwd_kv_outer.restype = i
+    lib.fa_fwd_kv_outer.argtypes = [vp] * 5 + [i] * 4 + [f, i, vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_kv_outer_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_kv_outer_workspace_size.argtypes = [i] * 4
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [i]
     _lib = lib
@@ -105,6 +109,20 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal,
                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
                                      int(B), int(H), int(N), int(d), float(scale),
                                      int(bool(causal)), _stream(stream)))
+
+
+def fa_fwd_kv_outer(q, k, v, o, lse, B, H, N, d, scale, causal, workspace, workspace_bytes,
+                    stream=None) -> int:
+    """Enqueue the key/value-outer (Algorithm 1 order) forward pass; pointers
+    may be ints or tensors.  Returns the fa_status code."""
+    return int(load_library().fa_fwd_kv_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                              int(B), int(H), int(N), int(d), float(scale),
+                                              int(bool(causal)), _ptr(workspace),
+                                              int(workspace_bytes), _stream(stream)))
+
+
+def fa_fwd_kv_outer_workspace_size(B, H, N, d) -> int:
+    return int(load_library().fa_fwd_kv_outer_workspace_size(int(B), int(H), int(N), int(d)))
 
 
 def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace,
@@ -217,6 +235,34 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, ws, need, stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return o, lse
+
+
+def forward_kv_outer(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Torch convenience wrapper of fa_fwd_kv_outer (bf16 [B, H, N, d] device
+    tensors): allocates O, LSE and the fp32 state workspace, returns (O, LSE)."""
+    import torch
+
+    if not (q.shape == k.shape == v.shape and q.dim() == 4):
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise TypeError("q, k, v must be bfloat16")
+    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_fwd_kv_outer_workspace_size(B, H, N, d)
+    if need == 0:
+        raise FAError(FA_ERR_SHAPE, fa_strerror(FA_ERR_SHAPE))
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_fwd_kv_outer(q, k, v, o, lse, B, H, N, d, scale, causal, ws, need, stream)
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return o, lse

@@ -82,6 +82,22 @@ uint64_t decode_workspace(int B, int H, int Nq, int d, int S, uint64_t *lse_offs
     return o_bytes + rows * 4;
 }
 
+// O [B,H,N,d] then l, m [B,H,N], fp32, each part 256-byte aligned.
+uint64_t kvouter_workspace(int B, int H, int N, int d, uint64_t *l_off, uint64_t *m_off) {
+    const uint64_t rows = (uint64_t)B * H * N;
+    const uint64_t o_bytes = (rows * d * 4 + 255) / 256 * 256;
+    const uint64_t v_bytes = (rows * 4 + 255) / 256 * 256;
+    if (l_off) *l_off = o_bytes;
+    if (m_off) *m_off = o_bytes + v_bytes;
+    return o_bytes + 2 * v_bytes;
+}
+
+bool fwd_shape_ok(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || N > (1 << 30) || (d != 64 && d != 128)) return false;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    return bh <= ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d);
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,6 +127,32 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
     if (rc != FA_OK) return rc;
     const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
                                              d, scale, causal != 0, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_kv_outer_workspace_size(int B, int H, int N, int d) {
+    if (!fwd_shape_ok(B, H, N, d)) return 0;
+    return (size_t)kvouter_workspace(B, H, N, d, nullptr, nullptr);
+}
+
+int fa_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int H, int N, int d, float scale, int causal, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2);
+    if (rc != FA_OK) return rc;
+    uint64_t l_off = 0, m_off = 0;
+    const uint64_t need = kvouter_workspace(B, H, N, d, &l_off, &m_off);
+    if (!workspace || (uint64_t)workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return FA_ERR_ALIGN;
+    const uint64_t rows = (uint64_t)B * H * N;
+    const uint64_t t_bytes = rows * d * 2;
+    for (const void *p : {q, k, v, (const void *)o})
+        if (overlaps(workspace, need, p, t_bytes)) return FA_ERR_ALIAS;
+    if (overlaps(workspace, need, lse, rows * 4)) return FA_ERR_ALIAS;
+    char *ws = static_cast<char *>(workspace);
+    const hipError_t e = fa::launch_fwd_kvouter_bf16(
+        q, k, v, o, lse, B, H, N, d, scale, causal != 0, reinterpret_cast<float *>(ws),
+        reinterpret_cast<float *>(ws + l_off), reinterpret_cast<float *>(ws + m_off), stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -38,152 +38,10 @@
 #include <cmath>
 
 #include "fa_internal.h"
+#include "fa_tiles.h"
 
 namespace fa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-#define LDS3 __attribute__((address_space(3)))
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 32;            // queries (dq) or keys (dkdv) per wave
-constexpr int kOuter = kWaves * kRowsPerWave;  // rows owned by one workgroup
-constexpr int kInner = 64;                  // rows per streamed tile
-constexpr float kLog2e = 1.4426950408889634f;
-
-// One swizzle for tiles read both by 128-bit row reads (16 rows x one 16-byte
-// chunk per LDS pass) and by the 64-bit transpose read (4 rows x 4 chunks per
-// pass): the stored chunk of logical chunk c in row r is c ^ swz(r).
-//   d = 128 (one row per 256-byte line): swz = 4(r & 3) + ((r >> 2) & 3);
-//   d = 64  (two rows per line):         swz = 4((r >> 1) & 1) + ((r >> 2) & 3).
-// Both depend on r mod 16 only.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// Workgroup id -> (batch*head, tile): consecutive ids go to consecutive XCDs,
-// and XCD x walks the contiguous range [x*W/8, (x+1)*W/8) of (head, tile)
-// pairs when the grid divides evenly (its L2 then serves one head's stream).
-__device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse, int &bh,
-                                          int &tile) {
-    int gidx = L;
-    if ((W & 7) == 0) gidx = (L & 7) * (W >> 3) + (L >> 3);
-    bh = gidx / ntiles;
-    tile = gidx - bh * ntiles;
-    if (reverse) tile = ntiles - 1 - tile;
-}
-
-// Direct-to-LDS copy of one kInner-row tile of a [N, D] bf16 matrix (rows r0
-// .. r0 + kInner - 1; rows >= N read as zeros) into `dst`, swizzled: lane l of
-// load u of wave w writes chunk position q = (u*kWaves + w)*64 + l, and
-// fetches the logical chunk that the swizzle stores there.  Load u is 4 KiB
-// (16 or 32 rows) after load 0 on both sides and leaves the row's swizzle
-// term unchanged, so one lane offset `src` (load 0) serves every load.
-template <int D>
-__device__ __forceinline__ void load_tile(const __bf16 *mat, int N, int r0, LDS3 char *dst,
-                                          uint32_t src, int wave) {
-    constexpr int kLoads = kInner * (D / 8) / kThreads;
-    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - r0)) * (uint32_t)(D * 2);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat + (size_t)r0 * D, bytes);
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)(dst + (u * kWaves + wave) * 1024),
-                                                 16, src, u * kWaves * 1024, 0, 0);
-}
-
-// Direct-to-LDS copy of vec[c0 .. c0 + 63] (fp32; entries at or past N read
-// as 0) into dst[0 .. 63], one 4-byte load per lane of the calling wave.
-__device__ __forceinline__ void load_vec(const float *vec, int N, int c0, LDS3 float *dst,
-                                         int lane) {
-    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - c0)) * 4u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vec + c0, bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
-}
-
-// Lane source offset of load_tile's first load (see there).
-template <int D>
-__device__ __forceinline__ uint32_t tile_src_offset(int wave, int lane) {
-    const int q = wave * 64 + lane;
-    const int r = q / (D / 8);
-    const int p = q % (D / 8);
-    return (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
-}
-
-// Byte offset (within a tile) of the 128-bit operand read of k-step ks: lane
-// (g, i) reads row i (+32 per 32-row block) and logical chunk 2ks + g.  The
-// stored chunk is (2ks + g) ^ swz(i) = (g ^ swz(i)) ^ 2ks, so the offset is
-// the k-step-0 offset with the chunk field XOR-ed by 32 ks bytes.
-template <int D>
-__device__ __forceinline__ uint32_t row_read_offset(int lane) {
-    const int g = lane >> 5, i = lane & 31;
-    return (uint32_t)(i * D * 2 + ((g ^ swz<D>(i)) << 4));
-}
-__device__ __forceinline__ uint32_t row_read_at(uint32_t base, int ks) {
-    return base ^ (uint32_t)(ks << 5);
-}
-
-// Byte offsets of the transpose reads that form the A operand M^T (M = a
-// tile, [row][d]) of a 32 (d) x 16 (rows) MFMA block: in 16-lane group
-// G = lane/16 (m0 = 16 (G & 1), g = G >> 1), lane i of the group reads the
-// four bf16 of row 16T + 8h + 4g + i/4, columns 32db + m0 + 4(i%4) .. +3; the
-// two halves h = 0, 1 form one 8-element operand.  The swizzle term depends on
-// h (not on T), so each h has its own offset; d-block db only adds 4db to
-// the logical chunk, i.e. XORs the chunk field with 64 db bytes.
-template <int D>
-__device__ __forceinline__ void tr_read_offsets(int lane, uint32_t *off) {
-    const int g = lane >> 5, gi = lane & 15, m0 = 16 * ((lane >> 4) & 1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = 8 * h + 4 * g + (gi >> 2);
-        const int col = m0 + 4 * (gi & 3);
-        const int c = col >> 3;
-        off[h] = (uint32_t)(row * D * 2 + ((c ^ swz<D>(row)) << 4) + ((col & 4) << 1));
-    }
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8 tr_read(const LDS3 char *tile, const uint32_t *off, int T,
-                                          int db) {
-    const LDS3 char *base = tile + T * 16 * D * 2;
-    const uint32_t x = (uint32_t)(db << 6);
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + (off[0] ^ x)));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + (off[1] ^ x)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-__device__ __forceinline__ u32x4 load16(const __bf16 *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
-}
-
-// Store a [D x 32] accumulator block set (lane (g, j) holds row `row` of the
-// result, columns 32db + 8a + 4g + e in acc[db][4a + e]) times `mul` as bf16.
-template <int D>
-__device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, float mul, int g) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * mul;
-            *reinterpret_cast<bf16x4 *>(row_ptr + 32 * db + 8 * a + 4 * g) =
-                __builtin_convertvector(x, bf16x4);
-        }
-}
 
 // ---------------------------------------------------------------------------
 // dq kernel: one workgroup = 128 queries of one (batch, head); wave w owns

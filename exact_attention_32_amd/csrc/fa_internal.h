@@ -23,6 +23,14 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            float *delta, int B, int H, int N, int d, float scale, bool causal,
                            hipStream_t stream);
 
+// Forward pass in the key/value-outer order of Algorithm 1: one launch per
+// 64-key block; ows [B,H,N,d], lws, mws [B,H,N] (fp32) carry O, l, m between
+// launches.
+hipError_t launch_fwd_kvouter_bf16(const void *q, const void *k, const void *v, void *o,
+                                   float *lse, int B, int H, int N, int d, float scale,
+                                   bool causal, float *ows, float *lws, float *mws,
+                                   hipStream_t stream);
+
 // Decode (few queries over many keys, key axis split in chunks).
 constexpr int kDecodeMaxQueries = 16;
 constexpr int kDecodeMinChunk = 64;       // keys per chunk, at least

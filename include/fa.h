@@ -159,6 +159,32 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
  * invalid shapes). */
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
 
+/*
+ * fa_fwd_kv_outer -- the same result as fa_fwd (O and LSE, bf16 in/out) in
+ * the loop order of Algorithm 1 of "解析 FlashAttention（2）：FlashAttention-v1
+ * 前向传播" (section 4): key/value blocks outside, query blocks inside, the
+ * output O and the statistics l, m written back to device memory after every
+ * step (lines 12-13) and read again at the next one (line 8).  It exists to
+ * measure that order against fa_fwd's (query blocks outside, which the
+ * unit-12 loop-order lesson of "在线 Softmax 与 FlashAttention" shows gives
+ * the same O without those round trips).
+ *
+ * One kernel launch per 64-key block j is enqueued on `stream`; each covers
+ * the 128-row query blocks that can see block j.  Per (i, j) it computes the
+ * block statistics with the block's own maximum (line 10), merges them with
+ * the stored ones (line 11) and rescales the stored, normalised O_i
+ * (line 12).  The state O, l, m is fp32 in the caller's workspace (at least
+ * fa_fwd_kv_outer_workspace_size bytes; contents on return unspecified; no
+ * overlap with any other argument).  Arguments, shapes and errors otherwise
+ * as for fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+int fa_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fa_fwd_kv_outer needs (0 for invalid shapes). */
+size_t fa_fwd_kv_outer_workspace_size(int B, int H, int N, int d);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_strerror(int status);
 

@@ -161,3 +161,23 @@ def test_decode_validation_codes(lib):
     assert call(ws=DK) == fa.FA_ERR_ALIAS
     assert call(o=DQ) == fa.FA_ERR_ALIAS
     assert call(lse=DW + 64) == fa.FA_ERR_ALIAS
+
+
+def test_kv_outer_validation_and_size(lib):
+    ws = fa.fa_fwd_kv_outer_workspace_size
+    assert ws(1, 1, 100, 64) >= 100 * 64 * 4 + 2 * 100 * 4
+    assert ws(2, 3, 100, 128) > ws(1, 3, 100, 128)
+    assert ws(1, 1, 0, 64) == 0 and ws(1, 1, 10, 80) == 0
+    W = BASE + 7 * GAP
+
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, ws=W, wsb=1 << 30)
+        a.update(kw)
+        return fa.fa_fwd_kv_outer(a["q"], a["k"], a["v"], a["o"], a["lse"], 2, 3, 100, 64, 0.125,
+                                  1, a["ws"], a["wsb"], None)
+    assert call(q=0) == fa.FA_ERR_NULL
+    assert call(ws=0) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=1024) == fa.FA_ERR_WORKSPACE
+    assert call(ws=W + 8) == fa.FA_ERR_ALIGN
+    assert call(ws=K) == fa.FA_ERR_ALIAS
+    assert call(ws=L - 64) == fa.FA_ERR_ALIAS
