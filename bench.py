@@ -335,6 +335,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default=None,
+                    help="forward pass: run the workload's shape in this type (fa_fwd_ex)")
+    ap.add_argument("--layout", choices=("bhnd", "bnhd"), default="bhnd",
+                    help="forward pass: memory order of q, k, v, o ([B,N,H,d] goes through "
+                         "fa_fwd_ex as strided views)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode", "kvouter"),
                     default="fwd")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -367,6 +372,8 @@ def main() -> int:
         return bench_decode(args)
     name = args.workload or inputs.HEADLINE
     w = inputs.WORKLOADS[name]
+    if args.dtype and args.dtype != w.dtype:
+        w = w.with_shape(dtype=args.dtype, name=f"{w.name}_as_{args.dtype}")
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_qkv(w)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
@@ -380,6 +387,21 @@ def main() -> int:
         rc = fn(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, stream)
         if rc != fa.FA_OK:
             raise fa.FAError(rc, fa.fa_strerror(rc))
+
+    if args.which == "fwd" and (w.dtype == "f16" or args.layout == "bnhd"):
+        if w.dtype == "f32":
+            raise SystemExit("fa_fwd_ex takes bf16 or fp16")
+        if args.layout == "bnhd":
+            qd, kd, vd, o = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+                             for t in (qd, kd, vd, o))
+        ex_strides = [x for t in (qd, kd, vd, o) for x in t.stride()[:3]]
+        ex_dtype = fa.FA_DTYPE_FP16 if w.dtype == "f16" else fa.FA_DTYPE_BF16
+
+        def step():  # noqa: F811
+            rc = fa.fa_fwd_ex(ex_dtype, qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale,
+                              w.causal, ex_strides, stream)
+            if rc != fa.FA_OK:
+                raise fa.FAError(rc, fa.fa_strerror(rc))
 
     if args.which == "kvouter":
         if w.dtype != "bf16":
@@ -443,7 +465,8 @@ def main() -> int:
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    # bf16 and fp16 share the dense MFMA peak
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
     metric = "attention fwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -472,6 +495,7 @@ def main() -> int:
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "inputs": w.dist, "pass": args.which,
+                   "layout": args.layout,
                    "flops_per_step": flops,
                    "pct_mfma_peak": round(100 * tflops / peak, 2)},
         "roofline": roofline,

@@ -22,9 +22,13 @@ FA_ERR_ALIGN = 5
 FA_ERR_HIP = 6
 FA_ERR_ALIAS = 7
 FA_ERR_WORKSPACE = 8
+FA_ERR_DTYPE = 9
+FA_ERR_STRIDE = 10
+FA_DTYPE_BF16 = 0
+FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_bwd", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
-           "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size", "fa_strerror")
+EXPORTS = ("fa_bwd", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_ex",
+           "fa_fwd_f32", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size", "fa_strerror")
 
 _lib = None
 
@@ -56,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode.argtypes = [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t, vp]
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_decode_workspace_size.argtypes = [i] * 6
+    lib.fa_fwd_ex.restype = i
+    lib.fa_fwd_ex.argtypes = [i] + [vp] * 5 + [i] * 4 + [f, i, ctypes.POINTER(ctypes.c_int64), vp]
     lib.fa_fwd_kv_outer.restype = i
     lib.fa_fwd_kv_outer.argtypes = [vp] * 5 + [i] * 4 + [f, i, vp, ctypes.c_size_t, vp]
     lib.fa_fwd_kv_outer_workspace_size.restype = ctypes.c_size_t
@@ -111,6 +117,18 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal,
                                      int(bool(causal)), _stream(stream)))
 
 
+def fa_fwd_ex(dtype, q, k, v, o, lse, B, H, N, d, scale, causal, strides, stream=None) -> int:
+    """Enqueue the forward pass on bf16 or fp16 strided views.  ``strides``
+    is a sequence of 12 element strides (q, k, v, o: batch, head, row), or
+    None for a NULL pointer.  Returns the fa_status code."""
+    arr = None
+    if strides is not None:
+        arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    return int(load_library().fa_fwd_ex(int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        int(B), int(H), int(N), int(d), float(scale),
+                                        int(bool(causal)), arr, _stream(stream)))
+
+
 def fa_fwd_kv_outer(q, k, v, o, lse, B, H, N, d, scale, causal, workspace, workspace_bytes,
                     stream=None) -> int:
     """Enqueue the key/value-outer (Algorithm 1 order) forward pass; pointers
@@ -142,32 +160,44 @@ def fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits=0) -> int:
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
             stream=None):
-    """Torch convenience wrapper: q, k, v are contiguous [B, H, N, d] device
-    tensors, all bf16 or all fp32.  Allocates O (input dtype) and LSE (fp32,
-    [B, H, N]) unless given, enqueues the kernel on ``stream`` (default: the
-    current torch stream) and returns (O, LSE).  ``scale`` defaults to
-    1/sqrt(d), the factor of the attention definition."""
+    """Torch convenience wrapper: q, k, v are [B, H, N, d] device tensors, all
+    bf16, all fp16 or all fp32.  bf16 and fp16 may be strided views whose last
+    dimension is contiguous (fa_fwd_ex; dense bf16 goes to fa_fwd); fp32 must
+    be contiguous (fa_fwd_f32).  Allocates O (input dtype, dense) and LSE
+    (fp32, [B, H, N]) unless given, enqueues the kernel on ``stream``
+    (default: the current torch stream) and returns (O, LSE).  ``scale``
+    defaults to 1/sqrt(d), the factor of the attention definition."""
     import torch
 
     if not (q.shape == k.shape == v.shape and q.dim() == 4):
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("q, k, v must all be bfloat16 or all be float32")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16,
+                                                             torch.float32):
+        raise TypeError("q, k, v must all be bfloat16, all float16 or all float32")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
-    rc = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    dense = all(t.is_contiguous() for t in (q, k, v, out))
+    if q.dtype == torch.float32:
+        if not dense:
+            raise ValueError("float32 tensors must be contiguous")
+        rc = fa_fwd_f32(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    elif q.dtype == torch.bfloat16 and dense:
+        rc = fa_fwd(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    else:
+        if any(t.stride(3) != 1 for t in (q, k, v, out)):
+            raise ValueError("the last dimension must be contiguous")
+        strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
+        dt = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+        rc = fa_fwd_ex(dt, q, k, v, out, lse, B, H, N, d, scale, causal, strides, stream)
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return out, lse

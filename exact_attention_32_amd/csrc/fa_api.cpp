@@ -3,6 +3,7 @@
 // is enqueued; no HIP runtime call is made for an invalid argument list.
 #include "fa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -98,6 +99,28 @@ bool fwd_shape_ok(int B, int H, int N, int d) {
     return bh <= ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d);
 }
 
+// Byte span of a strided [B, H, N, d] view of 2-byte elements: one past the
+// last byte any element occupies.
+uint64_t view_span(const int64_t *s, int B, int H, int N, int d) {
+    return ((uint64_t)(B - 1) * s[0] + (uint64_t)(H - 1) * s[1] + (uint64_t)(N - 1) * s[2] + d) * 2u;
+}
+
+// Rows of a strided view do not overlap: with the (extent > 1) dimensions
+// sorted by stride, each stride reaches past everything the smaller ones
+// cover (a row covers d elements).
+bool rows_disjoint(const int64_t *s, int B, int H, int N, int d) {
+    struct Dim { int64_t stride; int64_t extent; };
+    Dim dims[3] = {{s[0], B}, {s[1], H}, {s[2], N}};
+    std::sort(dims, dims + 3, [](const Dim &a, const Dim &b) { return a.stride < b.stride; });
+    int64_t covered = d;  // elements spanned by the dimensions so far, from a row start
+    for (const Dim &x : dims) {
+        if (x.extent <= 1) continue;
+        if (x.stride < covered) return false;
+        covered = x.stride * (x.extent - 1) + covered;
+    }
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +150,42 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
     if (rc != FA_OK) return rc;
     const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
                                              d, scale, causal != 0, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_ex(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int N, int d, float scale, int causal, const int64_t *strides,
+              hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !strides) return FA_ERR_NULL;
+    if (!fwd_shape_ok(B, H, N, d)) {
+        if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
+        if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+        return FA_ERR_SHAPE;
+    }
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;
+    for (int t = 0; t < 4; ++t) {
+        const int64_t *st = strides + 3 * t;
+        if (st[0] < 0 || st[1] < 0 || st[2] < d || st[2] > (1 << 24)) return FA_ERR_STRIDE;
+        if (st[0] > (int64_t)1 << 50 || st[1] > (int64_t)1 << 50) return FA_ERR_STRIDE;
+    }
+    for (const void *p : {q, k, v, (const void *)o, (const void *)lse})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    for (int t = 0; t < 12; ++t)
+        if (strides[t] % 8) return FA_ERR_ALIGN;
+    if (!rows_disjoint(strides + 9, B, H, N, d)) return FA_ERR_STRIDE;
+    const uint64_t o_span = view_span(strides + 9, B, H, N, d);
+    const uint64_t l_bytes = (uint64_t)B * H * N * 4u;
+    const void *ins[3] = {q, k, v};
+    for (int t = 0; t < 3; ++t) {
+        const uint64_t span = view_span(strides + 3 * t, B, H, N, d);
+        if (overlaps(o, o_span, ins[t], span) || overlaps(lse, l_bytes, ins[t], span))
+            return FA_ERR_ALIAS;
+    }
+    if (overlaps(o, o_span, lse, l_bytes)) return FA_ERR_ALIAS;
+    const hipError_t e = fa::launch_fwd_ex(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B, H, N, d,
+                                           scale, causal != 0,
+                                           strides, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -207,6 +266,8 @@ const char *fa_strerror(int status) {
         case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";
         case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL or smaller than required";
+        case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_BF16 or FA_DTYPE_FP16";
+        case FA_ERR_STRIDE: return "FA_ERR_STRIDE: strides must be >= 0, row strides in [d, 2^24], output rows disjoint";
         default: return "unknown fa status code";
     }
 }

@@ -70,6 +70,29 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Element type of Q, K, V, O -- bf16 or fp16 -- with its gfx950 MFMA
+// (32 x 32 x 16, fp32 accumulation) and vector types.
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+    typedef bf16x8 x8;
+    typedef bf16x4 x4;
+    static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elem<_Float16> {
+    typedef f16x8 x8;
+    typedef f16x4 x4;
+    static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -124,7 +147,7 @@ __device__ __forceinline__ void map_block(int L, int W, int nqt, bool heavy_firs
     if (heavy_first) qt = nqt - 1 - qt;
 }
 
-__device__ __forceinline__ u32x4 load16(const __bf16 *p) {
+__device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
@@ -143,28 +166,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // behind them before it can start its MFMAs.  (Kept out of the kernel's
 // lambdas: a buffer descriptor local in a lambda makes the host pass drop the
 // kernel's launch stub.)
-template <int D, int kLoads>
-__device__ __forceinline__ void issue_tile_load(int i, const __bf16 *Kh, const __bf16 *Vh, int N,
-                                                int c0, LDS3 char *dk, LDS3 char *dv,
+// Strided views (STRIDED): rows of K and V are kn and vn elements apart; the
+// descriptor then ends after the last valid row's d elements.
+template <int D, int kLoads, bool STRIDED, typename E>
+__device__ __forceinline__ void issue_tile_load(int i, const E *Kh, const E *Vh, int N, int c0,
+                                                LDS3 char *dk, LDS3 char *dv,
                                                 const uint32_t *k_src, const uint32_t *v_src,
-                                                int wave) {
-    const uint32_t bytes = (uint32_t)min(kBc, N - c0) * (uint32_t)(D * 2);
+                                                int wave, int kn, int vn) {
     const int u = i >> 1;
     const int pos = (u * kWaves + wave) * 64 * 16;  // byte offset of this wave's 1 KiB
-    if ((i & 1) == 0) {
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
+    if constexpr (!STRIDED) {
+        const uint32_t bytes = (uint32_t)min(kBc, N - c0) * (uint32_t)(D * 2);
+        if ((i & 1) == 0) {
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
+        } else {
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
+        }
     } else {
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
+        const uint32_t rows = (uint32_t)min(kBc, N - c0);
+        if ((i & 1) == 0) {
+            const uint32_t bytes = (rows - 1) * (uint32_t)kn * 2u + (uint32_t)(D * 2);
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * kn, bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
+        } else {
+            const uint32_t bytes = (rows - 1) * (uint32_t)vn * 2u + (uint32_t)(D * 2);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * vn, bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
+        }
     }
 }
 
-template <int D, bool CAUSAL>
+// Element strides of strided views (d is contiguous); LSE stays [B, H, N].
+struct FwdStrides {
+    long long qb, qh, kb, kh, vb, vh, ob, oh;
+    int qn, kn, vn, on, H;
+};
+
+template <typename E, int D, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-                const __bf16 *__restrict__ V, __bf16 *__restrict__ O,
-                float *__restrict__ LSE, int N, int nqt, float scale, float scale_log2) {
+fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+           E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, float scale,
+           float scale_log2, FwdStrides st) {
+    typedef typename Elem<E>::x8 X8;
+    typedef typename Elem<E>::x4 X4;
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int kChunksPerRow = D / 8;                        // 16-byte chunks
     constexpr int kLoads = kBc * kChunksPerRow / kThreads;     // per thread per tile
@@ -186,20 +232,35 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     int bh, qt;
     map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
     const int r0 = qt * kBr;
-    const size_t hoff = (size_t)bh * (size_t)N * D;
-    const __bf16 *Qh = Q + hoff;
-    const __bf16 *Kh = K + hoff;
-    const __bf16 *Vh = V + hoff;
+    size_t qoff, koff, voff, ooff;
+    int qn, kn, vn, on;
+    if constexpr (STRIDED) {
+        const int b = bh / st.H, h = bh - b * st.H;
+        qoff = (size_t)(b * st.qb + h * st.qh);
+        koff = (size_t)(b * st.kb + h * st.kh);
+        voff = (size_t)(b * st.vb + h * st.vh);
+        ooff = (size_t)(b * st.ob + h * st.oh);
+        qn = st.qn;
+        kn = st.kn;
+        vn = st.vn;
+        on = st.on;
+    } else {
+        qoff = koff = voff = ooff = (size_t)bh * (size_t)N * D;
+        qn = kn = vn = on = D;
+    }
+    const E *Qh = Q + qoff;
+    const E *Kh = K + koff;
+    const E *Vh = V + voff;
     const int wrow0 = r0 + wave * kRowsPerWave;
     const int qrow = wrow0 + j;
 
     // Q^T as the B operand: lane (g, j) holds query qrow, columns 16ks+8g..+7.
-    bf16x8 qop[D / 16];
+    X8 qop[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (qrow < N) x = load16(Qh + (size_t)qrow * D + 16 * ks + 8 * g);
-        qop[ks] = __builtin_bit_cast(bf16x8, x);
+        if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
+        qop[ks] = __builtin_bit_cast(X8, x);
     }
 
     const int kv_end = CAUSAL ? min(N, r0 + kBr) : N;
@@ -216,8 +277,8 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         const int q = (u * kWaves + wave) * 64 + lane;
         const int r = q / kChunksPerRow;
         const int p = q % kChunksPerRow;
-        k_src[u] = (uint32_t)(r * D * 2 + ((p ^ k_swz<D>(r)) << 4));
-        v_src[u] = (uint32_t)(r * D * 2 + ((p ^ v_swz<D>(r)) << 4));
+        k_src[u] = (uint32_t)(r * kn * 2 + ((p ^ k_swz<D>(r)) << 4));
+        v_src[u] = (uint32_t)(r * vn * 2 + ((p ^ v_swz<D>(r)) << 4));
     }
     // The 2 kLoads tile loads are spread evenly over the D/16 k-steps of S.
     constexpr int kLoadStride = (D / 16) / (2 * kLoads);
@@ -266,7 +327,8 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         const int c0 = t * kBc;
         const bool prefetch = t + 1 < n_tiles;
         auto load = [&](int i) __attribute__((always_inline)) {
-            issue_tile_load<D, kLoads>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src, wave);
+            issue_tile_load<D, kLoads, STRIDED>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src, wave,
+                                                kn, vn);
         };
 
         // A wave whose rows all precede this tile has nothing to add.
@@ -285,12 +347,12 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
             // All K fragments of the tile are requested before the first MFMA,
             // so the LDS latency is paid once per tile, not once per k-step.
-            bf16x8 kf[D / 16][kBc / 32];
+            X8 kf[D / 16][kBc / 32];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
-                    kf[ks][kb] = *reinterpret_cast<const LDS3 bf16x8 *>(
+                    kf[ks][kb] = *reinterpret_cast<const LDS3 X8 *>(
                         kt + k_rd[ks] + kb * 32 * D * 2);
             __builtin_amdgcn_sched_barrier(0);
             // The S MFMAs run at raised wave priority: the other wave on this
@@ -303,8 +365,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qop[ks], s[kb], 0,
-                                                                    0, 0);
+                    s[kb] = Elem<E>::mfma(kf[ks][kb], qop[ks], s[kb]);
                 if (prefetch && ks % kLoadStride == 0) load(ks / kLoadStride);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -314,7 +375,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             // All V^T fragments of the tile are requested now; the softmax below
             // covers their latency.  Fragment (T, db) is two transpose reads
             // (keys 16T+4g+k and 16T+8+4g+k, columns of d-block db).
-            bf16x8 vf[kBc / 16][D / 32];
+            X8 vf[kBc / 16][D / 32];
 #pragma unroll
             for (int T = 0; T < kBc / 16; ++T)
 #pragma unroll
@@ -324,7 +385,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     const v4i16 hi =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
                     vf[T][db] = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
 
             // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
@@ -367,7 +428,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             const float mc = m_use * scale_log2;
 
             // P = exp(scale*(s - m)) = 2^(s*scale*log2e - m*scale*log2e).
-            bf16x8 pop[kBc / 16];
+            X8 pop[kBc / 16];
             float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < kBc / 32; ++kb) {
@@ -379,8 +440,8 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     rs += lo[r];
                     rs += hi[r];
                 }
-                pop[2 * kb] = __builtin_convertvector(lo, bf16x8);
-                pop[2 * kb + 1] = __builtin_convertvector(hi, bf16x8);
+                pop[2 * kb] = __builtin_convertvector(lo, X8);
+                pop[2 * kb + 1] = __builtin_convertvector(hi, X8);
             }
             l_run = l_run * alpha + rs;
             // Rescale the accumulator first, then add this tile's P V.
@@ -397,8 +458,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int T = 0; T < kBc / 16; ++T)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[T][db], pop[T], acc[db], 0,
-                                                                      0, 0);
+                    acc[db] = Elem<E>::mfma(vf[T][db], pop[T], acc[db]);
         }
 
         // The next tile's loads must have landed before anyone reads them, and
@@ -409,7 +469,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
 #pragma unroll
     for (int i = 0; i < 2 * kLoads; ++i)
-        issue_tile_load<D, kLoads>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave);
+        issue_tile_load<D, kLoads, STRIDED>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave, kn, vn);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < n_tiles; t += 2) {
@@ -426,7 +486,7 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     }
     const float inv = 1.f / l_tot;
     if (qrow < N) {
-        __bf16 *orow = O + hoff + (size_t)qrow * D;
+        E *orow = O + ooff + (size_t)qrow * on;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -434,24 +494,35 @@ fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
-                *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * a + 4 * g) =
-                    __builtin_convertvector(x, bf16x4);
+                *reinterpret_cast<X4 *>(orow + 32 * db + 8 * a + 4 * g) =
+                    __builtin_convertvector(x, X4);
             }
         if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse,
-                  int B, int H, int N, float scale, hipStream_t stream) {
+template <typename E, int D, bool CAUSAL, bool STRIDED>
+hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                  int N, float scale, const FwdStrides &st, hipStream_t stream) {
     const int nqt = (N + kBr - 1) / kBr;
     const int blocks = B * H * nqt;
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream,
-                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-                       static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), lse, N, nqt,
-                       scale, scale_log2);
+    hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<const E *>(q), static_cast<const E *>(k),
+                       static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, scale,
+                       scale_log2, st);
     return hipGetLastError();
+}
+
+template <typename E, bool STRIDED>
+hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                    int N, int d, float scale, bool causal, const FwdStrides &st,
+                    hipStream_t stream) {
+    if (d == 64)
+        return causal ? launch<E, 64, true, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream)
+                      : launch<E, 64, false, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream);
+    return causal ? launch<E, 128, true, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream)
+                  : launch<E, 128, false, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream);
 }
 
 }  // namespace
@@ -459,11 +530,28 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int N, int d, float scale, bool causal,
                            hipStream_t stream) {
-    if (d == 64)
-        return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                      : launch<64, false>(q, k, v, o, lse, B, H, N, scale, stream);
-    return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                  : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+    const FwdStrides none = {};
+    return launch_e<__bf16, false>(q, k, v, o, lse, B, H, N, d, scale, causal, none, stream);
+}
+
+hipError_t launch_fwd_ex(bool fp16, const void *q, const void *k, const void *v, void *o,
+                         float *lse, int B, int H, int N, int d, float scale, bool causal,
+                         const int64_t *strides, hipStream_t stream) {
+    const int64_t *sq = strides, *sk = strides + 3, *sv = strides + 6, *so = strides + 9;
+    const long long hd = (long long)N * d, bd = (long long)H * hd;
+    bool dense = true;
+    for (const int64_t *t : {sq, sk, sv, so}) dense = dense && t[0] == bd && t[1] == hd && t[2] == d;
+    FwdStrides st;
+    st.qb = sq[0]; st.qh = sq[1]; st.qn = (int)sq[2];
+    st.kb = sk[0]; st.kh = sk[1]; st.kn = (int)sk[2];
+    st.vb = sv[0]; st.vh = sv[1]; st.vn = (int)sv[2];
+    st.ob = so[0]; st.oh = so[1]; st.on = (int)so[2];
+    st.H = H;
+    if (fp16)
+        return dense ? launch_e<_Float16, false>(q, k, v, o, lse, B, H, N, d, scale, causal, st, stream)
+                     : launch_e<_Float16, true>(q, k, v, o, lse, B, H, N, d, scale, causal, st, stream);
+    return dense ? launch_e<__bf16, false>(q, k, v, o, lse, B, H, N, d, scale, causal, st, stream)
+                 : launch_e<__bf16, true>(q, k, v, o, lse, B, H, N, d, scale, causal, st, stream);
 }
 
 }  // namespace fa

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -11,6 +12,12 @@ namespace fa {
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                            float *lse, int B, int H, int N, int d, float scale,
                            bool causal, hipStream_t stream);
+
+// bf16 (fp16 = false) or fp16 views with element strides (q, k, v, o: batch,
+// head, row; d contiguous); the dense layout takes the contiguous kernels.
+hipError_t launch_fwd_ex(bool fp16, const void *q, const void *k, const void *v, void *o,
+                         float *lse, int B, int H, int N, int d, float scale, bool causal,
+                         const int64_t *strides, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o,
                           float *lse, int B, int H, int N, int d, float scale,

@@ -37,7 +37,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str          # "f32" or "bf16"
+    dtype: str          # "f32", "bf16" or "f16"
     dist: str           # "normal", "normal4" or "uniform"
     causal: bool
     seed: int
@@ -72,7 +72,7 @@ HEADLINE = "w3_bf16_b2h32_n8192_d128_causal"
 
 
 def torch_dtype(dtype: str):
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
 
 
 def make_qkv(w: Workload, device="cpu"):

@@ -47,6 +47,7 @@
 #define FA_H_
 
 #include <hip/hip_runtime_api.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -61,8 +62,14 @@ enum fa_status {
     FA_ERR_ALIGN = 5,    /* a pointer is not 16-byte aligned                 */
     FA_ERR_HIP = 6,      /* the kernel launch failed (hipGetLastError)       */
     FA_ERR_ALIAS = 7,    /* an output overlaps an input or another output    */
-    FA_ERR_WORKSPACE = 8 /* workspace NULL or smaller than required          */
+    FA_ERR_WORKSPACE = 8,/* workspace NULL or smaller than required          */
+    FA_ERR_DTYPE = 9,    /* unknown element type                             */
+    FA_ERR_STRIDE = 10   /* strides invalid (row stride < d or > 2^24,       */
+                         /* negative, or an output whose rows overlap)       */
 };
+
+/* Element types of fa_fwd_ex. */
+enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
 
 /*
  * fa_fwd -- bf16 inputs and output, fp32 accumulation.
@@ -158,6 +165,30 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
 /* Bytes of workspace fa_decode needs for these arguments (0 if they are
  * invalid shapes). */
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/*
+ * fa_fwd_ex -- fa_fwd generalised to fp16 as well as bf16 tensors, and to
+ * strided views, as the Triton page's kernel takes per-tensor strides
+ * ("手写 FlashAttention", section 3.4, its kernel's parameter list).
+ *
+ *   dtype   : FA_DTYPE_BF16 or FA_DTYPE_FP16 -- the type of q, k, v and o
+ *             (the MFMA products use that type's gfx950 instruction;
+ *             probabilities are rounded to it before P.V; accumulation,
+ *             scores and statistics are fp32; o is rounded to nearest even)
+ *   strides : host array of 12 element strides, for q, k, v, o in turn:
+ *             batch, head, row.  The d elements of a row are contiguous.
+ *             Element (b, h, n, t) of q is q[b*s0 + h*s1 + n*s2 + t].
+ *             Row strides must lie in [d, 2^24], every stride must be >= 0
+ *             and a multiple of 8 (16-byte rows); input strides may be 0
+ *             (e.g. k, v shared by all heads); o's rows must not overlap
+ *             each other.  lse stays a dense fp32 [B, H, N].
+ * Other arguments and errors as for fa_fwd, plus FA_ERR_DTYPE and
+ * FA_ERR_STRIDE.  No part of o may overlap q, k, v or lse.  With the dense
+ * strides of [B, H, N, d] and dtype bf16 this runs exactly fa_fwd's kernel.
+ */
+int fa_fwd_ex(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int N, int d, float scale, int causal,
+              const int64_t *strides, hipStream_t stream);
 
 /*
  * fa_fwd_kv_outer -- the same result as fa_fwd (O and LSE, bf16 in/out) in

@@ -39,11 +39,12 @@ def test_status_codes_match_header():
 
 
 def test_strerror(lib):
-    for code in range(9):
+    for code in range(11):
         s = fa.fa_strerror(code)
         assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM",
                              "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP",
-                             "FA_ERR_ALIAS", "FA_ERR_WORKSPACE"][code])
+                             "FA_ERR_ALIAS", "FA_ERR_WORKSPACE", "FA_ERR_DTYPE",
+                             "FA_ERR_STRIDE"][code])
     assert "unknown" in fa.fa_strerror(99)
     assert "unknown" in fa.fa_strerror(-1)
 
@@ -181,3 +182,37 @@ def test_kv_outer_validation_and_size(lib):
     assert call(ws=W + 8) == fa.FA_ERR_ALIGN
     assert call(ws=K) == fa.FA_ERR_ALIAS
     assert call(ws=L - 64) == fa.FA_ERR_ALIAS
+
+
+def test_fwd_ex_validation_codes(lib):
+    B, H, N, d = 2, 3, 100, 64
+    dense = [H * N * d, N * d, d] * 4
+    bshd = [N * H * d, d, H * d] * 4           # [B, N, H, d] memory order
+
+    def call(dtype=fa.FA_DTYPE_BF16, strides=dense, **kw):
+        p = dict(q=Q, k=K, v=V, o=O, lse=L)
+        p.update(kw)
+        return fa.fa_fwd_ex(dtype, p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, N, d, 0.125,
+                            1, strides, None)
+    assert call(strides=None) == fa.FA_ERR_NULL
+    assert call(q=0) == fa.FA_ERR_NULL
+    assert call(dtype=2) == fa.FA_ERR_DTYPE
+    assert call(dtype=-1) == fa.FA_ERR_DTYPE
+    bad = list(dense); bad[2] = 32                 # q row stride < d
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[5] = 1 << 25            # k row stride > 2^24
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[0] = -8
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[1] = N * d + 4          # not a multiple of 8 elements
+    assert call(strides=bad) == fa.FA_ERR_ALIGN
+    bad = list(dense); bad[9:12] = [H * N * d, 8 * d, d]   # o heads overlap (8 rows apart)
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[9:12] = [0, N * d, d]           # o batches on top of each other
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    shared = list(dense); shared[3:5] = [N * d, 0]         # k shared by all heads: allowed
+    shared[6:8] = [N * d, 0]
+    assert call(strides=shared, o=Q) == fa.FA_ERR_ALIAS    # (fails on the alias only)
+    assert call(strides=bshd, o=K + 64) == fa.FA_ERR_ALIAS
+    assert call(strides=bshd, lse=V + 1024) == fa.FA_ERR_ALIAS
+    assert call(strides=bshd, q=Q + 8) == fa.FA_ERR_ALIGN

@@ -1,0 +1,131 @@
+"""fa_fwd_ex on the GPU: fp16 tensors and strided views, through the C ABI.
+
+fp16 gates follow from the bf16 ones by the ratio of the two types' unit
+roundoffs (2^-8 / 2^-11 = 8): the errors that matter are the rounding of P
+before P.V and of the output, both relative to the element type, so the bf16
+gates 2e-2 (max-abs) and 5e-3 (relative L2) become 2.5e-3 and 6.25e-4.  LSE
+is fp32 either way: <= 1e-3.  A strided bf16 view must give exactly the bits
+of fa_fwd on a dense copy (the same kernel arithmetic, other addresses).
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_32_amd as fa
+from exact_attention_32_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+GATES = {"bf16": (2e-2, 5e-3), "f16": (2.5e-3, 6.25e-4)}
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def check(o, lse, o_ref, lse_ref, dtype, what):
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"{what}: non-finite"
+    max_abs = float(np.abs(o - o_ref).max())
+    rel = float(np.linalg.norm((o - o_ref).ravel()) / np.linalg.norm(o_ref.ravel()))
+    lse_err = float(np.abs(lse - lse_ref).max())
+    _say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse={lse_err:.3e}")
+    ga, gr = GATES[dtype]
+    assert max_abs <= ga and rel <= gr and lse_err <= 1e-3, what
+
+
+F16 = [
+    (1, 1, 1, 64, "normal", False),
+    (1, 2, 63, 128, "normal", True),
+    (2, 1, 65, 64, "uniform", True),
+    (1, 3, 129, 128, "normal4", True),
+    (2, 2, 300, 64, "normal", False),
+    (1, 2, 1000, 128, "normal", True),
+    (1, 1, 2048, 64, "normal4", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dist,causal", F16)
+def test_fp16_dense(B, H, N, d, dist, causal, oracle_lib):
+    w = inputs.Workload(f"f16_{B}x{H}x{N}x{d}_{dist}_{int(causal)}", B, H, N, d, "f16", dist,
+                        causal, seed=5000 + N + d)
+    _say(f"case {w.name}")
+    q, k, v = inputs.make_qkv(w)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_lib.attention(q, k, v, w.scale, causal)
+    check(o, lse, o_ref, lse_ref, "f16", w.name)
+
+
+def _views(q, k, v, layout):
+    """Strided views of the same values: 'bshd' ([B, N, H, d] memory order),
+    'padded' (rows d + 64 elements apart), 'mixed' (q bshd, k padded, v dense)."""
+    def bshd(t):
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    def padded(t):
+        B, H, N, d = t.shape
+        big = torch.zeros(B, H, N, d + 64, dtype=t.dtype, device=t.device)
+        big[..., :d] = t
+        return big[..., :d]
+    if layout == "bshd":
+        return bshd(q), bshd(k), bshd(v)
+    if layout == "padded":
+        return padded(q), padded(k), padded(v)
+    return bshd(q), padded(k), v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("layout", ["bshd", "padded", "mixed"])
+@pytest.mark.parametrize("N,d,causal", [(300, 64, True), (257, 128, False), (1000, 128, True)])
+def test_strided_views_match_dense(dtype, layout, N, d, causal):
+    w = inputs.Workload("sv", 2, 3, N, d, dtype, "normal", causal, seed=N + d)
+    q, k, v = (t.cuda() for t in inputs.make_qkv(w))
+    qs, ks, vs = _views(q, k, v, layout)
+    assert not qs.is_contiguous() or layout == "mixed"
+    o1, l1 = fa.forward(q, k, v, causal=causal, scale=w.scale)
+    o2, l2 = fa.forward(qs, ks, vs, causal=causal, scale=w.scale)
+    # strided output as well: O written into the first d columns of wider rows
+    big = torch.full((2, 3, N, d + 32), 7.0, dtype=q.dtype, device="cuda")
+    o3, l3 = fa.forward(qs, ks, vs, causal=causal, scale=w.scale, out=big[..., :d])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), f"{dtype} {layout}: strided != dense"
+    assert torch.equal(o1, o3) and torch.equal(l1, l3), f"{dtype} {layout}: strided output"
+    assert torch.all(big[..., d:] == 7.0), "wrote outside the output view"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_shared_kv_heads(dtype, oracle_lib):
+    """K and V given once and shared by every head (head stride 0)."""
+    w = inputs.Workload("mq", 2, 4, 500, 128, dtype, "normal", True, seed=77)
+    q, k, v = inputs.make_qkv(w)
+    k1, v1 = k[:, :1], v[:, :1]
+    kx, vx = k1.expand(2, 4, 500, 128), v1.expand(2, 4, 500, 128)
+    o, lse = fa.forward(q.cuda(), kx.cuda(), vx.cuda(), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_lib.attention(q, kx.contiguous(), vx.contiguous(), w.scale, True)
+    check(o, lse, o_ref, lse_ref, dtype, f"shared kv {dtype}")
+
+
+def test_fp16_headline_shape_sampled(oracle_lib):
+    w = inputs.WORKLOADS["w3_bf16_b2h32_n8192_d128_causal"].with_shape(dtype="f16",
+                                                                        name="w3_f16")
+    q, k, v = inputs.make_qkv(w)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(w, 256)
+    o_ref, lse_ref = oracle_lib.attention_rows(q, k, v, w.scale, True, rows)
+    o = o.cpu()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lse = lse.cpu()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    check(o, lse, o_ref, lse_ref, "f16", "w3 shape fp16 sampled")
+
+
+def test_fwd_ex_error_codes_on_device():
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.float16, device="cuda")
+    k, v, o = torch.zeros_like(q), torch.zeros_like(q), torch.empty_like(q)
+    lse = torch.empty(1, 1, 64, device="cuda")
+    dense = [64 * 64, 64 * 64, 64] * 4
+    assert fa.fa_fwd_ex(7, q, k, v, o, lse, 1, 1, 64, 64, 0.125, 0, dense, None) == fa.FA_ERR_DTYPE
+    assert fa.fa_fwd_ex(fa.FA_DTYPE_FP16, q, k, v, q, lse, 1, 1, 64, 64, 0.125, 0, dense,
+                        None) == fa.FA_ERR_ALIAS
