@@ -121,13 +121,33 @@ constexpr float kRescaleLog2 = 8.f;
 // instruction lands at LDS byte 16*l after the instruction's base, so the
 // swizzle is applied on the global (gather) side.  Rows beyond N are outside
 // the buffer's range and arrive as zeros.
+//   d = 32 and d = 96 (also measured layouts of the same two read patterns,
+//   checked conflict-free by enumeration):
+//     K tile, d = 32 (four rows per 256-byte line): chunk c stored at
+//       c ^ ((r >> 2) & 3);
+//     K tile, d = 96 (192-byte rows, 12 chunks, where an XOR would leave the
+//       row): chunk c stored at (c + 3 ((r >> 2) & 3)) mod 12;
+//     V tile, d = 32 and 96: unswizzled (4 rows x 4 chunks already fall on 16
+//       distinct bank groups, as 4r and 12r mod 16 step through multiples of 4).
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
-    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : D == 32 ? ((r >> 2) & 3) : 0;
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
-    return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+    return D == 128 ? 4 * (r & 3) : D == 64 ? 2 * (r & 3) : 0;
+}
+// Stored chunk of logical chunk c in row r of a K tile, and the logical chunk
+// stored at position p (the gather side of the tile copy).
+template <int D>
+__device__ __forceinline__ int k_stored(int r, int c) {
+    if constexpr (D == 96) return (c + 3 * ((r >> 2) & 3)) % 12;
+    else return c ^ k_swz<D>(r);
+}
+template <int D>
+__device__ __forceinline__ int k_logical(int r, int p) {
+    if constexpr (D == 96) return (p + 12 - 3 * ((r >> 2) & 3)) % 12;
+    else return p ^ k_swz<D>(r);
 }
 
 #define LDS3 __attribute__((address_space(3)))
@@ -211,7 +231,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
            float scale_log2, FwdStrides st) {
     typedef typename Elem<E>::x8 X8;
     typedef typename Elem<E>::x4 X4;
-    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(D == 32 || D == 64 || D == 96 || D == 128, "head dim");
     constexpr int kChunksPerRow = D / 8;                        // 16-byte chunks
     constexpr int kLoads = kBc * kChunksPerRow / kThreads;     // per thread per tile
     // Two buffers per operand as four distinct objects: the tile loop is
@@ -277,7 +297,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
         const int q = (u * kWaves + wave) * 64 + lane;
         const int r = q / kChunksPerRow;
         const int p = q % kChunksPerRow;
-        k_src[u] = (uint32_t)(r * kn * 2 + ((p ^ k_swz<D>(r)) << 4));
+        k_src[u] = (uint32_t)(r * kn * 2 + (k_logical<D>(r, p) << 4));
         v_src[u] = (uint32_t)(r * vn * 2 + ((p ^ v_swz<D>(r)) << 4));
     }
     // The 2 kLoads tile loads are spread evenly over the D/16 k-steps of S.
@@ -290,7 +310,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     uint32_t k_rd[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-        k_rd[ks] = (uint32_t)(j * D * 2 + (((2 * ks + g) ^ k_swz<D>(j)) << 4));
+        k_rd[ks] = (uint32_t)(j * D * 2 + (k_stored<D>(j, 2 * ks + g) << 4));
     // V^T (A operand of O^T += V^T P^T) through the 16-lane transpose read:
     // in group G = lane/16 (m0 = 16*(G&1), g = G>>1), lane i of the group reads
     // row 16T + 8h + 4g + i/4, columns 32db + m0 + 4(i%4) .. +3.  The row's
@@ -514,15 +534,23 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
     return hipGetLastError();
 }
 
+template <typename E, int D, bool STRIDED>
+hipError_t launch_c(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                    int N, float scale, bool causal, const FwdStrides &st, hipStream_t stream) {
+    return causal ? launch<E, D, true, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream)
+                  : launch<E, D, false, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream);
+}
+
 template <typename E, bool STRIDED>
 hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                     int N, int d, float scale, bool causal, const FwdStrides &st,
                     hipStream_t stream) {
-    if (d == 64)
-        return causal ? launch<E, 64, true, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream)
-                      : launch<E, 64, false, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream);
-    return causal ? launch<E, 128, true, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream)
-                  : launch<E, 128, false, STRIDED>(q, k, v, o, lse, B, H, N, scale, st, stream);
+    switch (d) {
+        case 32: return launch_c<E, 32, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
+        case 64: return launch_c<E, 64, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
+        case 96: return launch_c<E, 96, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
+        default: return launch_c<E, 128, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
+    }
 }
 
 }  // namespace

@@ -22,7 +22,7 @@ constexpr int kRows = 128;  // query rows (= threads) per workgroup
 // Keys per LDS tile: 32 at d = 64; 16 at d = 128 so that q, the accumulator
 // and the tile's scores fit the 256 vector registers without spilling.
 template <int D>
-constexpr int tile_keys() { return D == 128 ? 16 : 32; }
+constexpr int tile_keys() { return D >= 96 ? 16 : 32; }
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kRows)
@@ -134,14 +134,22 @@ hipError_t launch(const float *q, const float *k, const float *v, float *o, floa
 
 }  // namespace
 
+template <int D>
+hipError_t launch_c(const float *q, const float *k, const float *v, float *o, float *lse, int B,
+                    int H, int N, float scale, bool causal, hipStream_t stream) {
+    return causal ? launch<D, true>(q, k, v, o, lse, B, H, N, scale, stream)
+                  : launch<D, false>(q, k, v, o, lse, B, H, N, scale, stream);
+}
+
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                           int B, int H, int N, int d, float scale, bool causal,
                           hipStream_t stream) {
-    if (d == 64)
-        return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                      : launch<64, false>(q, k, v, o, lse, B, H, N, scale, stream);
-    return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                  : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+    switch (d) {
+        case 32: return launch_c<32>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        case 64: return launch_c<64>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        case 96: return launch_c<96>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        default: return launch_c<128>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+    }
 }
 
 }  // namespace fa

@@ -33,7 +33,9 @@
  *            in fp32.  (The pages keep the row maximum m and sum l, first
  *            page, section 4, last steps of Algorithm 1; this library returns
  *            the single number m*scale + ln(l) instead.)
- * Shapes:    B, H, N >= 1; N <= 2^30; d is 64 or 128; B*H*N*d < 2^40.
+ * Shapes:    B, H, N >= 1; N <= 2^30; B*H*N*d < 2^40; the head dim d is
+ *            32, 64, 96 or 128 for the forward entry points (fa_fwd,
+ *            fa_fwd_f32, fa_fwd_ex) and 64 or 128 for the others.
  * scale:     finite and > 0 (usually 1/sqrt(d)).
  * causal:    0 = no mask, any other value = top-left causal mask.
  * Errors:    all argument checks run before anything is enqueued; a failed
@@ -57,7 +59,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = 1,     /* a required pointer is NULL                       */
     FA_ERR_SHAPE = 2,    /* B, H or N < 1, N > 2^30, or B*H*N*d >= 2^40      */
-    FA_ERR_HEADDIM = 3,  /* d is not 64 or 128                               */
+    FA_ERR_HEADDIM = 3,  /* d not supported by the entry point (see Shapes)  */
     FA_ERR_SCALE = 4,    /* scale is not finite, or not > 0                  */
     FA_ERR_ALIGN = 5,    /* a pointer is not 16-byte aligned                 */
     FA_ERR_HIP = 6,      /* the kernel launch failed (hipGetLastError)       */

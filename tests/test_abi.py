@@ -74,8 +74,10 @@ def test_validation_codes(fn, lib):
     assert _call(fn, N=0) == fa.FA_ERR_SHAPE
     assert _call(fn, N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
     assert _call(fn, B=1 << 16, H=1 << 10, N=1 << 10) == fa.FA_ERR_SHAPE  # 2^42 elements
-    for d in (0, 16, 32, 48, 96, 127, 256):
+    for d in (0, 16, 48, 80, 127, 256):
         assert _call(fn, d=d) == fa.FA_ERR_HEADDIM
+    for d in (32, 96):   # forward head dims beyond 64 and 128: fail later, on the scale
+        assert _call(fn, d=d, scale=0.0) == fa.FA_ERR_SCALE
     for s in (0.0, -0.125, float("inf"), float("nan")):
         assert _call(fn, scale=s) == fa.FA_ERR_SCALE
     assert _call(fn, q=Q + 8) == fa.FA_ERR_ALIGN
@@ -118,7 +120,8 @@ def test_bwd_validation_codes(lib):
         assert _bwd(**{name: 0}) == fa.FA_ERR_NULL, name
     assert _bwd(B=0) == fa.FA_ERR_SHAPE
     assert _bwd(N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
-    assert _bwd(d=96) == fa.FA_ERR_HEADDIM
+    assert _bwd(d=96) == fa.FA_ERR_HEADDIM       # the backward pass takes 64 and 128
+    assert _bwd(d=32) == fa.FA_ERR_HEADDIM
     assert _bwd(scale=float("nan")) == fa.FA_ERR_SCALE
     assert _bwd(scale=0.0) == fa.FA_ERR_SCALE
     assert _bwd(dk=BDK + 8) == fa.FA_ERR_ALIGN

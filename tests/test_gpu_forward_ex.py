@@ -129,3 +129,49 @@ def test_fwd_ex_error_codes_on_device():
     assert fa.fa_fwd_ex(7, q, k, v, o, lse, 1, 1, 64, 64, 0.125, 0, dense, None) == fa.FA_ERR_DTYPE
     assert fa.fa_fwd_ex(fa.FA_DTYPE_FP16, q, k, v, q, lse, 1, 1, 64, 64, 0.125, 0, dense,
                         None) == fa.FA_ERR_ALIAS
+
+
+HEAD_DIMS = [
+    # (B, H, N, d, dtype, dist, causal)
+    (1, 2, 1, 32, "bf16", "normal", True),
+    (2, 2, 200, 32, "bf16", "normal", False),
+    (1, 3, 333, 32, "bf16", "normal4", True),
+    (1, 2, 1000, 32, "f16", "uniform", True),
+    (1, 1, 1, 96, "bf16", "normal", False),
+    (1, 2, 65, 96, "bf16", "normal", True),
+    (2, 2, 300, 96, "bf16", "normal4", False),
+    (1, 2, 1000, 96, "bf16", "uniform", True),
+    (1, 2, 777, 96, "f16", "normal", True),
+    (1, 2, 130, 32, "f32", "normal", True),
+    (1, 2, 257, 96, "f32", "normal", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,dist,causal", HEAD_DIMS)
+def test_head_dims(B, H, N, d, dtype, dist, causal, oracle_lib):
+    """Head dims 32 and 96 (the forward kernels' other layouts)."""
+    w = inputs.Workload(f"hd_{B}x{H}x{N}x{d}_{dtype}_{dist}_{int(causal)}", B, H, N, d, dtype,
+                        dist, causal, seed=6000 + N + d)
+    _say(f"case {w.name}")
+    q, k, v = inputs.make_qkv(w)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_lib.attention(q, k, v, w.scale, causal)
+    if dtype == "f32":
+        err = float(np.abs(o.cpu().double().numpy() - o_ref).max())
+        _say(f"  {w.name}: max_abs={err:.3e}")
+        assert err <= 1e-5
+        assert float(np.abs(lse.cpu().double().numpy() - lse_ref).max()) <= 1e-3
+    else:
+        check(o, lse, o_ref, lse_ref, dtype, w.name)
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_head_dims_strided_match_dense(d):
+    w = inputs.Workload("hds", 2, 3, 400, d, "bf16", "normal", True, seed=d)
+    q, k, v = (t.cuda() for t in inputs.make_qkv(w))
+    qs, ks, vs = _views(q, k, v, "bshd")
+    o1, l1 = fa.forward(q, k, v, causal=True, scale=w.scale)
+    o2, l2 = fa.forward(qs, ks, vs, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
