@@ -40,6 +40,10 @@ Counter helpers (used to produce the summaries under profiles/):
   python bench.py --summarize-counters FDIR WDIR WORKLOAD CMD
                                                   traffic summary of the
                                                   FETCH_SIZE / WRITE_SIZE runs
+  python bench.py --summarize-pmc KERNEL_SUBSTRING TRACE_DIR CMD DIR [DIR ...]
+                                                  per-dispatch SQ/GRBM counters
+                                                  of one kernel, with the mean
+                                                  duration from a kernel trace
 """
 from __future__ import annotations
 
@@ -329,6 +333,47 @@ def bench_decode(args) -> int:
     return 0
 
 
+def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
+    """Per-dispatch averages of the counters collected in the `--pmc` runs
+    under `dirs` for the kernels whose name contains `kernel`, and derived
+    figures.  GRBM_GUI_ACTIVE is the sum over the 8 XCDs of each XCD's active
+    cycles; SQ_VALU_MFMA_BUSY_CYCLES the sum over the 1024 SIMDs of their
+    matrix-core busy cycles (32 per 32x32x16 MFMA).  Hence the shader clock
+    = GRBM_GUI_ACTIVE / 8 / mean duration (from the kernel trace in
+    `trace_dir`), the MFMA-busy fraction = SQ_VALU_MFMA_BUSY_CYCLES /
+    (1024 * GRBM_GUI_ACTIVE / 8), and the same busy cycles against 2.4 GHz."""
+    vals = {}
+    for d in dirs:
+        for name, counter, value in _db_rows(
+                d, "select kernel_name, counter_name, value from counters_collection"):
+            if kernel in name:
+                vals.setdefault(counter, []).append(value)
+    durs = [avg for name, _, _, avg, _ in _db_rows(
+        trace_dir, "select name, total_calls, total_duration, average, percentage from top_kernels")
+        if kernel in name]
+    print(f"COMMAND: {command}")
+    print(f"KERNEL: {kernel}")
+    print("counter | dispatches | mean per dispatch")
+    mean = {}
+    for c in sorted(vals):
+        mean[c] = sum(vals[c]) / len(vals[c])
+        print(f"{c} | {len(vals[c])} | {mean[c]:.6g}")
+    xcd_cycles = mean.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+    if durs:
+        us = durs[0]
+        print(f"MEAN_DURATION_US (kernel trace): {us:.2f}")
+        if xcd_cycles:
+            print(f"SHADER_CLOCK_GHZ: {xcd_cycles / (us * 1e3):.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            print(f"MFMA_BUSY_FRACTION_AT_2.4GHZ: "
+                  f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * us * 1e-6 * 2.4e9):.3f}")
+    if xcd_cycles and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+        print(f"MFMA_BUSY_FRACTION: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * xcd_cycles):.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_ACTIVE_INST_LDS" in mean and mean["SQ_ACTIVE_INST_LDS"]:
+        print(f"LDS_BANK_CONFLICT_PER_LDS_ACTIVE_CYCLE: "
+              f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_ACTIVE_INST_LDS']:.4f}")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +393,7 @@ def main() -> int:
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "WORKLOAD", "COMMAND"))
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -355,6 +401,10 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return 0
+    if args.summarize_pmc:
+        a = args.summarize_pmc
+        summarize_pmc(a[0], a[1], a[2], a[3:])
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
