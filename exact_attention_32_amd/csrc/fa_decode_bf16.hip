@@ -82,21 +82,28 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float *acc, floa
     m = mn;
 }
 
-// One workgroup (one wave) = one (batch*head, key chunk).  Writes the
-// chunk's normalised partial output and LSE (0 and -inf for a query that
-// sees no key of the chunk).
+// One workgroup = one (batch*head, key chunk), with one wave per group of
+// up to four queries: every wave streams the same K and V rows (the repeats
+// hit the caches of the compute unit) and keeps the online-softmax state of
+// its own queries only.  Writes the chunk's normalised partial output and
+// LSE (0 and -inf for a query that sees no key of the chunk).
+template <int NQ>
+constexpr int kDecodeWaves = (NQ + 3) / 4;
+
 template <int D, int NQ, bool CAUSAL>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64 * kDecodeWaves<NQ>)
 decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     const __bf16 *__restrict__ V, float *__restrict__ o_part,
                     float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
                     float scale_log2) {
     constexpr int G = D / 8;       // lanes per key row
     constexpr int RPW = 64 / G;    // rows per load instruction
-    constexpr int ROUNDS = NQ <= 2 ? 8 : (NQ <= 4 ? 4 : 2);
+    constexpr int NQW = NQ < 4 ? NQ : 4;  // queries per wave
+    constexpr int ROUNDS = NQW <= 2 ? 8 : 4;
     constexpr int BLK = RPW * ROUNDS;  // keys per block of loads
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int qbase = NQW * (threadIdx.x >> 6);  // first query of this wave
     const int grp = lane / G;
     const int col = lane % G;
     const int s = blockIdx.x % S;
@@ -104,21 +111,22 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int k0 = s * chunk;
     const int k1 = min(Nk, k0 + chunk);
 
-    // This lane's 8 columns of every query, widened to fp32.
-    float qf[NQ][8];
+    // This lane's 8 columns of every query of the wave, widened to fp32.
+    float qf[NQW][8];
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
+    for (int qi = 0; qi < NQW; ++qi) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (qi < Nq) w = *reinterpret_cast<const u32x4 *>(Q + ((size_t)bh * Nq + qi) * D + col * 8);
+        if (qbase + qi < Nq)
+            w = *reinterpret_cast<const u32x4 *>(Q + ((size_t)bh * Nq + qbase + qi) * D + col * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             qf[qi][2 * e] = bf16_lo(w[e]);
             qf[qi][2 * e + 1] = bf16_hi(w[e]);
         }
     }
-    float m[NQ], l[NQ], acc[NQ][8];
+    float m[NQW], l[NQW], acc[NQW][8];
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
+    for (int qi = 0; qi < NQW; ++qi) {
         m[qi] = -INFINITY;
         l[qi] = 0.f;
 #pragma unroll
@@ -139,12 +147,12 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             }
         }
         // Scores of the block's rows (identical in all G lanes of a group).
-        float sc[ROUNDS][NQ];
+        float sc[ROUNDS][NQW];
 #pragma unroll
         for (int r = 0; r < ROUNDS; ++r) {
             const int j = base + r * RPW + grp;
 #pragma unroll
-            for (int qi = 0; qi < NQ; ++qi) {
+            for (int qi = 0; qi < NQW; ++qi) {
                 float x = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -152,13 +160,13 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     x = __builtin_fmaf(qf[qi][2 * e + 1], bf16_hi(kr[r][e]), x);
                 }
                 x = group_sum<G>(x);
-                const bool hidden = j >= k1 || (CAUSAL && j > Nk - Nq + qi);
+                const bool hidden = j >= k1 || (CAUSAL && j > Nk - Nq + qbase + qi);
                 sc[r][qi] = hidden ? -INFINITY : x;
             }
         }
         // Online softmax of this group's stream, one update per block.
 #pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
+        for (int qi = 0; qi < NQW; ++qi) {
             float mb = sc[0][qi];
 #pragma unroll
             for (int r = 1; r < ROUNDS; ++r) mb = fmaxf(mb, sc[r][qi]);
@@ -188,7 +196,7 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
     // Merge the RPW group streams of the wave (lanes G, 2G, ... apart).
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
+    for (int qi = 0; qi < NQW; ++qi) {
 #pragma unroll
         for (int off = G; off < 64; off <<= 1) {
             const float mo = __shfl_xor(m[qi], off);
@@ -202,9 +210,9 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
     if (grp == 0) {
 #pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-            if (qi >= Nq) break;
-            const size_t prow = ((size_t)bh * S + s) * Nq + qi;
+        for (int qi = 0; qi < NQW; ++qi) {
+            if (qbase + qi >= Nq) break;
+            const size_t prow = ((size_t)bh * S + s) * Nq + qbase + qi;
             const float inv = l[qi] > 0.f ? 1.f / l[qi] : 0.f;
             float *dst = o_part + prow * D + col * 8;
 #pragma unroll
@@ -307,7 +315,8 @@ hipError_t launch_nq(const void *q, const void *k, const void *v, void *o, float
                      int H, int Nq, int Nk, int S, int chunk, float scale, float *o_part,
                      float *lse_part, hipStream_t stream) {
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL((decode_split_kernel<D, NQ, CAUSAL>), dim3(B * H * S), dim3(64), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, NQ, CAUSAL>), dim3(B * H * S),
+                       dim3(64 * kDecodeWaves<NQ>), 0, stream,
                        static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
                        static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk, scale,
                        scale_log2);
