@@ -1,5 +1,7 @@
-// fa_fwd_bf16.hip -- fused attention forward for gfx950, bf16 in / bf16 out,
-// fp32 scores, softmax statistics and accumulator.
+// fa_fwd_bf16.hip -- fused attention forward for gfx950: bf16 tensors (the
+// fa_fwd path) and, through the same template, fp16 tensors and strided
+// views (fa_fwd_ex); head dims 32, 64, 96 and 128; fp32 scores, softmax
+// statistics and accumulator.
 //
 // What is computed: O = softmax(scale * Q K^T [+ causal mask]) V per
 // (batch, head), with the per-row log-sum-exp, as defined on the page
@@ -11,7 +13,8 @@
 // unit-12 lesson "在线 Softmax 与 FlashAttention" (loop-order part), which
 // states both orders give the same result.
 //
-// Mapping onto CDNA4
+// Mapping onto CDNA4 (described for d = 128; d/16 k-steps and d/32 output
+// blocks otherwise, with the LDS layouts given at k_swz / v_swz below)
 // ------------------
 // * One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
 //   wave owns 32 rows for the whole key loop (Q, the output accumulator and
