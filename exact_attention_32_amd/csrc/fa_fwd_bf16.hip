@@ -45,11 +45,14 @@
 //   and only tiles that straddle the diagonal (or the ragged end of N) pay
 //   for the element-wise mask (unit-12 causal-mask lesson: skip / diagonal /
 //   past tiles).
-// * Lazy rescale: a row's exponent base moves to its running maximum only
-//   when that maximum has grown by more than 2^8 (in base-2 units of the
-//   scaled logits) since the base was set; the accumulator is rescaled
-//   (wave-uniform branch) only then.  Numerator and denominator share the
-//   base, so O and the LSE are the same as with the exact running maximum.
+// * Lazy base: a tile's probabilities are first computed against the row's
+//   current exponent base, without a row maximum.  Only when some half-row
+//   sum of the tile exceeds a bound (2^32 for bf16 probabilities, 2^15 for
+//   fp16 ones), or is not finite -- always so on the first tile, whose base
+//   is -inf -- does the wave take the slow path: row maximum, base moved to
+//   it, accumulator and sum rescaled, probabilities recomputed.  Numerator
+//   and denominator share the base, so O and the LSE are those of the exact
+//   running maximum; the softmax of a tile costs no maximum on the fast path.
 // * Grid: workgroups are dealt round-robin over the 8 XCDs; consecutive
 //   workgroup ids are remapped so that each XCD walks a contiguous range of
 //   heads (its 4 MB L2 then serves the K/V stream of one head to all its
@@ -102,9 +105,14 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                // keys per tile
-// Growth of a row's maximum (in log2 units of the scaled logits) tolerated
-// before the exponent base and the accumulator are rescaled.
-constexpr float kRescaleLog2 = 8.f;
+// Largest half-row probability sum of a tile accepted against the current
+// exponent base (every probability of the tile is then at most this): 2^32
+// for bf16 probabilities (fp32's exponent range), 2^15 for fp16 ones (whose
+// largest finite value is 65504).
+template <typename E>
+constexpr float kSumMax = 4294967296.f;
+template <>
+constexpr float kSumMax<_Float16> = 32768.f;
 
 // Shared-memory tiles.  Both are [kBc keys][D] row-major, unpadded; the
 // 16-byte chunks of a row are XOR-swizzled so that the MFMA operand reads hit
@@ -335,7 +343,8 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m_run = -INFINITY;  // running max of the raw scores of row qrow
+    float m_run = -INFINITY;  // exponent base of row qrow (raw score units)
+    float mc_run = -INFINITY; // the base in scaled log2 units (m_run * scale_log2)
     float l_run = 0.f;        // this half-wave's share of the running sum
 
     LDS3 char *const k0 = (LDS3 char *)lds_k0;
@@ -423,58 +432,61 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
                         if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
             }
 
-            // Tile row maximum: in-register, then across the two half-waves.
-            float mt = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < kBc / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
-                                                                 __float_as_uint(mt), false, false);
-                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            // Lazy rescale: the exponent base m_run moves to the new maximum only
-            // when the tile's maximum exceeds it by more than kRescaleLog2 (in
-            // log2 units of the scaled logits); otherwise the base is kept and
-            // the tile's probabilities are at most 2^kRescaleLog2 instead of 1.
-            // Numerator and denominator share the base, so O = acc / l and
-            // LSE = m_run*scale + ln(l) are unchanged, while the rescale of the
-            // accumulator (and its wave-wide branch) becomes rare.
-            const bool bump = m_run == -INFINITY ? mt != -INFINITY
-                                                 : (mt - m_run) * scale_log2 > kRescaleLog2;
-            const float m_new = bump ? mt : m_run;
-            // A row that has seen no visible key keeps base 0 (its terms are 0).
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            // alpha from the OLD base, before it is replaced (exactly 1 if kept).
-            const float alpha = bump ? __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2) : 1.f;
-            const float mc = m_use * scale_log2;
-
-            // P = exp(scale*(s - m)) = 2^(s*scale*log2e - m*scale*log2e).
+            // Fast path: probabilities against the current exponent base, with
+            // no row maximum.  The tile is accepted when every half-row sum is
+            // at most kSumMax (so every probability is); the test also rejects
+            // inf / NaN sums, in particular on the first tile, whose base is
+            // still -inf.  Numerator and denominator share the base, so
+            // O = acc / l and LSE = base*scale + ln(l) do not depend on where
+            // the base sits.
             X8 pop[kBc / 16];
             float rs = 0.f;
+            auto exps = [&](float mcx) __attribute__((always_inline)) {
+                rs = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < kBc / 32; ++kb) {
-                f32x8 lo, hi;
+                for (int kb = 0; kb < kBc / 32; ++kb) {
+                    f32x8 lo, hi;
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -mc));
-                    hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 8], scale_log2, -mc));
-                    rs += lo[r];
-                    rs += hi[r];
+                    for (int r = 0; r < 8; ++r) {
+                        lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -mcx));
+                        hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 8], scale_log2, -mcx));
+                        rs += lo[r];
+                        rs += hi[r];
+                    }
+                    pop[2 * kb] = __builtin_convertvector(lo, X8);
+                    pop[2 * kb + 1] = __builtin_convertvector(hi, X8);
                 }
-                pop[2 * kb] = __builtin_convertvector(lo, X8);
-                pop[2 * kb + 1] = __builtin_convertvector(hi, X8);
-            }
-            l_run = l_run * alpha + rs;
-            // Rescale the accumulator first, then add this tile's P V.
-            if (__ballot(alpha != 1.f)) {
+            };
+            exps(mc_run);
+            if (__ballot(!(rs <= kSumMax<E>))) {
+                // Slow path: the base moves to the row maximum (tile and
+                // running), the accumulator and sum are rescaled, and the
+                // tile's probabilities are recomputed against the new base.
+                float mt = s[0][0];
+#pragma unroll
+                for (int kb = 0; kb < kBc / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+                {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(
+                        __float_as_uint(mt), __float_as_uint(mt), false, false);
+                    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                }
+                const float m_new = fmaxf(m_run, mt);
+                // A row that has seen no visible key keeps base 0 (its terms are 0).
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = (m_run == -INFINITY) ? 0.f
+                                                         : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+                mc_run = m_use * scale_log2;
+                m_run = m_use;
+                l_run *= alpha;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                exps(mc_run);
             }
-            m_run = m_new;
+            l_run += rs;
 
             // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15.
 #pragma unroll

@@ -4,6 +4,7 @@ Gates (fixed by the method's specification):
   fp32 inputs : max |O_gpu - O_ref| <= 1e-5
   bf16 inputs : max |O_gpu - O_ref| <= 2e-2 and
                 ||O_gpu - O_ref||_2 / ||O_ref||_2 <= 5e-3 (over the whole tensor)
+  fp16 inputs : the bf16 gates divided by 8 (2.5e-3, 6.25e-4)
   LSE         : max |LSE_gpu - LSE_ref| <= 1e-3 in every case
 Both sides read the same rounded inputs; the oracle widens them to fp64.
 """
@@ -22,6 +23,9 @@ TOL_F32 = 1e-5
 TOL_BF16_ABS = 2e-2
 TOL_BF16_REL = 5e-3
 TOL_LSE = 1e-3
+# fp16 inputs: the bf16 gates divided by 8, the ratio of the unit roundoffs
+TOL_F16_ABS = 2.5e-3
+TOL_F16_REL = 6.25e-4
 
 
 def _say(msg):
@@ -45,6 +49,9 @@ def check(o, lse, o_ref, lse_ref, dtype, what):
     _say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse={lse_err:.3e}")
     if dtype == "f32":
         assert max_abs <= TOL_F32, f"{what}: max abs {max_abs}"
+    elif dtype == "f16":
+        assert max_abs <= TOL_F16_ABS, f"{what}: max abs {max_abs}"
+        assert rel <= TOL_F16_REL, f"{what}: rel-L2 {rel}"
     else:
         assert max_abs <= TOL_BF16_ABS, f"{what}: max abs {max_abs}"
         assert rel <= TOL_BF16_REL, f"{what}: rel-L2 {rel}"
@@ -173,23 +180,30 @@ def test_error_codes_on_device():
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("order", ["growing", "shrinking"])
-def test_row_max_moves_across_tiles(order, causal, oracle_lib):
-    """Logits whose row maximum grows (or shrinks) by more than 2^8 from one
-    64-key tile to the next, so the exponent base of the online softmax is
-    moved and the accumulator rescaled at nearly every tile (and, in the
-    shrinking order, only at the first)."""
+@pytest.mark.parametrize("dtype,bits", [("bf16", 18.0), ("bf16", 40.0), ("f16", 10.0), ("f16", 20.0)])
+def test_row_max_moves_across_tiles(order, causal, dtype, bits, oracle_lib):
+    """Logits whose row maximum grows (or shrinks) by `bits` (log2 units of the
+    scaled logits) from one 64-key tile to the next.  The kernel keeps a row's
+    exponent base while every half-row probability sum of a tile stays within
+    2^32 (bf16) or 2^15 (fp16): growth above that bound forces the fallback
+    (row maximum, new base, rescale) at every tile; growth below it runs
+    several tiles on an old base, with probabilities far above 1, before one
+    falls back.  In the shrinking order the base is set at the first tile and
+    every later probability is small."""
     B, H, N, d = 1, 2, 700, 128
-    g = torch.Generator().manual_seed(41)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    # per-tile growth of max_j q.k_j * scale * log2(e) along the ramp below
+    top = bits * N * math.log(2) / (2.0 * d * scale * 64)
+    g = torch.Generator().manual_seed(41 + int(bits))
     u = torch.randint(0, 2, (d,), generator=g).float() * 2 - 1          # +-1 direction
-    ramp = torch.linspace(0.0, 6.0, N) if order == "growing" else torch.linspace(6.0, 0.0, N)
+    ramp = torch.linspace(0.0, top, N) if order == "growing" else torch.linspace(top, 0.0, N)
     q = 2.0 * u + 0.3 * torch.randn(B, H, N, d, generator=g)
     k = ramp[None, None, :, None] * u + 0.3 * torch.randn(B, H, N, d, generator=g)
     v = torch.randn(B, H, N, d, generator=g)
-    q, k, v = (t.to(torch.bfloat16).contiguous() for t in (q, k, v))
-    scale = float(np.float32(1 / math.sqrt(d)))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    q, k, v = (t.to(tdt).contiguous() for t in (q, k, v))
     o, lse = run_gpu(q, k, v, causal, scale)
     o_ref, lse_ref = oracle_lib.attention(q, k, v, scale, causal)
-    # logit growth per 64-key tile, in log2 units: must exceed the 2^8 slack
-    per_tile = 2.0 * d * scale * (6.0 / N) * 64 / math.log(2)
-    assert per_tile > 8, per_tile
-    check(o, lse, o_ref, lse_ref, "bf16", f"row max {order} causal={causal}")
+    per_tile = 2.0 * d * scale * (top / N) * 64 / math.log(2)
+    assert abs(per_tile - bits) < 1e-6, per_tile
+    check(o, lse, o_ref, lse_ref, dtype, f"row max {order} {dtype} {bits} bits/tile causal={causal}")
