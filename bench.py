@@ -341,7 +341,9 @@ def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
     matrix-core busy cycles (32 per 32x32x16 MFMA).  Hence the shader clock
     = GRBM_GUI_ACTIVE / 8 / mean duration (from the kernel trace in
     `trace_dir`), the MFMA-busy fraction = SQ_VALU_MFMA_BUSY_CYCLES /
-    (1024 * GRBM_GUI_ACTIVE / 8), and the same busy cycles against 2.4 GHz."""
+    (1024 * GRBM_GUI_ACTIVE / 8), and the same busy cycles against 2.4 GHz;
+    the VALU issue fraction = 4 * SQ_ACTIVE_INST_VALU (quad-cycles, MFMA issue
+    included) / (1024 * GRBM_GUI_ACTIVE / 8)."""
     vals = {}
     for d in dirs:
         for name, counter, value in _db_rows(
@@ -369,6 +371,9 @@ def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
                   f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * us * 1e-6 * 2.4e9):.3f}")
     if xcd_cycles and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
         print(f"MFMA_BUSY_FRACTION: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * xcd_cycles):.3f}")
+    if xcd_cycles and "SQ_ACTIVE_INST_VALU" in mean:
+        # SQ_ACTIVE_INST_VALU counts issue quad-cycles (4 clocks) summed over waves
+        print(f"VALU_ISSUE_FRACTION: {4 * mean['SQ_ACTIVE_INST_VALU'] / (1024 * xcd_cycles):.3f}")
     if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_ACTIVE_INST_LDS" in mean and mean["SQ_ACTIVE_INST_LDS"]:
         print(f"LDS_BANK_CONFLICT_PER_LDS_ACTIVE_CYCLE: "
               f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_ACTIVE_INST_LDS']:.4f}")
