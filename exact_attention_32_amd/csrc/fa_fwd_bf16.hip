@@ -13,8 +13,15 @@
 // unit-12 lesson "在线 Softmax 与 FlashAttention" (loop-order part), which
 // states both orders give the same result.
 //
-// Mapping onto CDNA4 (described for d = 128; d/16 k-steps and d/32 output
-// blocks otherwise, with the LDS layouts given at k_swz / v_swz below)
+// Two kernels share the operand layouts, LDS swizzles, softmax and grid
+// mapping described here: fwd_kernel (head dims 32, 64, 96) and
+// fwd_pipe_kernel (head dim 128), which reorders the work inside a wave
+// into a software pipeline and runs 8-wave workgroups; see its own comment
+// further down.
+//
+// Mapping onto CDNA4 (described for fwd_kernel at d = 128; d/16 k-steps and
+// d/32 output blocks otherwise, with the LDS layouts given at k_swz / v_swz
+// below)
 // ------------------
 // * One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
 //   wave owns 32 rows for the whole key loop (Q, the output accumulator and
@@ -62,6 +69,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "fa_internal.h"
 
@@ -536,16 +544,449 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined kernel (head dims 64 and 128), W waves of 32 query rows
+// per workgroup.
+//
+// Same operand layouts, LDS swizzles and lazy exponent base as fwd_kernel
+// above; what changes is the order of work inside a wave.  The key axis is
+// walked in 32-key half tiles h, and step h of a wave issues, as one
+// interleaved instruction stream,
+//   * the O^T += V^T P^T MFMAs of half tile h-1,
+//   * the S^T = K Q^T MFMAs of half tile h+1, and
+//   * the softmax of half tile h (VALU), whose scores came out of step h-1,
+// none of which depends on another within the step.  The matrix core then
+// runs while the same wave computes its exponentials, so the overlap no
+// longer depends on the two waves of a SIMD being in opposite phases; that
+// in turn allows workgroups of 8 waves (256 query rows), which halves the
+// L2 -> LDS tile stream per FLOP.  The LDS reads of a step's first two MFMA
+// pairs are issued at the end of the step before, so that no step starts
+// by waiting for LDS.
+//
+// Every step runs the same straight-line code (a wave past its last
+// visible key multiplies zero probabilities until the workgroup's tiles
+// run out, or leaves the loop once it has added its last probabilities;
+// a half tile with masked keys takes a short masking branch first), so the
+// accumulators keep their registers from step to step.
+//
+// Buffers: three per operand; K tile i and V tile i live in buffer i mod 3.
+// A 64-key tile spans two steps: tile step t (steps 2t+1, 2t+2) reads V(t)
+// and K(t+1) and copies K(t+3) and V(t+2) into the buffers of K(t) and
+// V(t-1), which were last read in tile step t-1.  One barrier at the top of
+// each tile step orders those overwrites; each wave's copies have landed
+// (vmcnt) before it meets the barrier, so a tile copied in tile step t is
+// visible to all waves from tile step t+1 on, one tile step before it is
+// read -- which lets the end of tile step t read ahead into tile step t+1.
+constexpr int kPipeBufs = 3;
+
+// One 16-byte direct-to-LDS load per lane (load u of this wave's share) of
+// a tile with `rows` valid rows at `base` (row stride rs elements), for a
+// workgroup of W waves.  Load u covers tile rows from u R on, R = 64 W / (D /
+// 8); at D = 64 and 128 the swizzle of a row depends on its index modulo 32
+// and 16 only, so the lane's gather offset `src` (that of load 0) serves
+// every load, with the descriptor's base moved to row u R and its size cut
+// to the rows that remain (the hardware range check, which covers the
+// vector offset only, then still turns every row at or past `rows` into
+// zeros; none remaining gives an empty range and a load of zeros only).
+template <int D, int W, bool STRIDED, typename E>
+__device__ __forceinline__ void tile_load(const E *base, int rows, int rs, LDS3 char *dst,
+                                          uint32_t src, int u, int wave) {
+    static_assert(D == 64 || D == 128, "row swizzle periodic in the load's row step");
+    constexpr int kRowsPerLoad = 64 * W / (D / 8);
+    const int pos = (u * W + wave) * 64 * 16;
+    const int left = rows - u * kRowsPerLoad;
+    uint32_t bytes = 0;
+    if (left > 0)
+        bytes = STRIDED ? (uint32_t)(left - 1) * (uint32_t)rs * 2u + (uint32_t)(D * 2)
+                        : (uint32_t)left * (uint32_t)(D * 2);
+    // (The size is wave-uniform; said explicitly, as the compiler may
+    // otherwise clamp it in a vector register and wrap the load in a loop
+    // over distinct descriptors.)
+    bytes = __builtin_amdgcn_readfirstlane(bytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)u * kRowsPerLoad * rs, bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS3 void *)(dst + pos), 16, src, 0, 0, 0);
+}
+
+template <typename E, int D, bool CAUSAL, bool STRIDED, int W>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+                E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, float scale,
+                float scale_log2, FwdStrides st) {
+    typedef typename Elem<E>::x8 X8;
+    typedef typename Elem<E>::x4 X4;
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(W == 4 || W == 8, "waves");
+    // Two workgroups share a compute unit at W = 4: their six tiles of each
+    // operand must fit its 160 KiB of LDS.
+    static_assert(W == 8 || 2 * 2 * kPipeBufs * kBc * D * 2 <= 160 * 1024, "LDS");
+    constexpr int kRows = W * kRowsPerWave;   // query rows per workgroup
+    constexpr int kChunksPerRow = D / 8;
+    constexpr int kLoads = kBc * kChunksPerRow / (64 * W);  // per operand and lane
+    constexpr int KS = D / 16;  // k-steps of S^T = K Q^T
+    constexpr int DB = D / 32;  // 32-wide d blocks of O^T
+    static_assert(2 * DB == KS, "one P V^T MFMA per K Q^T MFMA");
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k0[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k1[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_k2[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v0[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v1[kBc * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lds_v2[kBc * D];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int g = lane >> 5;
+    const int j = lane & 31;
+
+    int bh, qt;
+    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
+    const int r0 = qt * kRows;
+    size_t qoff, koff, voff, ooff;
+    int qn, kn, vn, on;
+    if constexpr (STRIDED) {
+        const int b = bh / st.H, h = bh - b * st.H;
+        qoff = (size_t)(b * st.qb + h * st.qh);
+        koff = (size_t)(b * st.kb + h * st.kh);
+        voff = (size_t)(b * st.vb + h * st.vh);
+        ooff = (size_t)(b * st.ob + h * st.oh);
+        qn = st.qn;
+        kn = st.kn;
+        vn = st.vn;
+        on = st.on;
+    } else {
+        qoff = koff = voff = ooff = (size_t)bh * (size_t)N * D;
+        qn = kn = vn = on = D;
+    }
+    const E *Qh = Q + qoff;
+    const E *Kh = K + koff;
+    const E *Vh = V + voff;
+    const int wrow0 = r0 + wave * kRowsPerWave;
+    const int qrow = wrow0 + j;
+
+    X8 qop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
+        qop[ks] = __builtin_bit_cast(X8, x);
+    }
+
+    const int kv_end = CAUSAL ? min(N, r0 + kRows) : N;
+    const int n_tiles = (kv_end + kBc - 1) / kBc;
+    // Row qrow sees keys 0 .. vis (the element mask below); the wave's rows
+    // see keys up to vis_max at most.
+    const int vis = CAUSAL ? min(qrow, N - 1) : N - 1;
+    const int vis_max = CAUSAL ? wrow0 + kRowsPerWave - 1 : N - 1;
+
+    // Gather offsets of the lane's first tile load (see tile_load).
+    uint32_t k_src, v_src;
+    {
+        const int q = wave * 64 + lane;
+        const int r = q / kChunksPerRow;
+        const int p = q % kChunksPerRow;
+        k_src = (uint32_t)(r * kn * 2 + (k_logical<D>(r, p) << 4));
+        v_src = (uint32_t)(r * vn * 2 + ((p ^ v_swz<D>(r)) << 4));
+    }
+    uint32_t k_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        k_rd[ks] = (uint32_t)(j * D * 2 + (k_stored<D>(j, 2 * ks + g) << 4));
+    const int gi = lane & 15;
+    const int m0 = 16 * ((lane >> 4) & 1);
+    uint32_t v_rd[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int row = 4 * g + (gi >> 2);
+        const int col = 32 * db + m0 + 4 * (gi & 3);
+        const int c = col >> 3;
+        v_rd[db] = (uint32_t)(row * D * 2 + ((c ^ v_swz<D>(row)) << 4) + ((col & 4) << 1));
+    }
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m_run = -INFINITY;   // exponent base of row qrow (raw score units)
+    float mc_run = -INFINITY;  // the base times scale * log2(e)
+    float l_run = 0.f;         // this half-wave's share of the running sum
+
+    LDS3 char *const kb[kPipeBufs] = {(LDS3 char *)lds_k0, (LDS3 char *)lds_k1,
+                                      (LDS3 char *)lds_k2};
+    LDS3 char *const vb[kPipeBufs] = {(LDS3 char *)lds_v0, (LDS3 char *)lds_v1,
+                                      (LDS3 char *)lds_v2};
+
+    // LDS reads of MFMA pair i of a step: the V^T fragment (i / DB, i % DB)
+    // of half `hv` of tile buffer vt (two transpose reads) and the K
+    // fragment of k-step i of half `hk` of tile buffer kt.
+    auto read_pair = [&](int i, const LDS3 char *kt, int hk, const LDS3 char *vt, int hv, X8 &vfr,
+                         X8 &kfr) __attribute__((always_inline)) {
+        const LDS3 char *base = vt + v_rd[i % DB] + (2 * hv + i / DB) * 16 * D * 2;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
+        vfr = __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        kfr = *reinterpret_cast<const LDS3 X8 *>(kt + k_rd[i] + hk * 32 * D * 2);
+    };
+
+    // Element r of a half tile's S^T block is key 32h + 8(r/4) + 4g + r%4 of
+    // query qrow; its P^T operands p[0], p[1] cover keys 32h .. +15 and
+    // 32h+16 .. +31 (k-steps of O^T += V^T P^T).
+    //
+    // Probabilities of one half tile against exponent base mcx (scaled log2
+    // units) as P^T operands, and their (half-wave) sum.
+    auto exps = [&](const f32x16 &s, float mcx, X8 (&p)[2]) __attribute__((always_inline)) {
+        f32x8 lo, hi;
+        float ra = 0.f, rb = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -mcx));
+            hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 8], scale_log2, -mcx));
+            ra += lo[r];
+            rb += hi[r];
+        }
+        p[0] = __builtin_convertvector(lo, X8);
+        p[1] = __builtin_convertvector(hi, X8);
+        return ra + rb;
+    };
+    // Slow path of the lazy base: the base moves to the row maximum, the
+    // accumulator and the sum are rescaled, the probabilities recomputed.
+    auto rebase = [&](const f32x16 &s, X8 (&p)[2]) __attribute__((always_inline)) {
+        float mt = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                             false, false);
+            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha =
+            (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+        mc_run = m_use * scale_log2;
+        m_run = m_use;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        return exps(s, mc_run, p);
+    };
+
+    // Step h.  (kt, hk): LDS tile buffer and half holding the K rows of half
+    // tile h+1; (vt, hv): those holding the V rows of half tile h-1;
+    // (ktn, hkn), (vtn, hvn): the same for step h+1, whose first two MFMA
+    // pairs' operands this step reads at its end.  vf0/kf0: this step's
+    // first two pairs' operands (in), the next step's (out).  sc: scores of
+    // half tile h (in), sn: scores of half tile h+1 (out); pp: P^T of half
+    // tile h-1 (in), pc: P^T of half tile h (out).  With LOADS, the step
+    // also issues the copies of K(t+3) into kload and V(t+2) into vload
+    // (t = the tile of half tile h).  Every buffer a step reads has been
+    // filled (possibly with zeros past kv_end), so steps outside the wave's
+    // visible range compute finite, discarded scores and add zero
+    // probabilities.
+    auto step = [&](int h, auto loads_tag, const LDS3 char *kt, int hk, const LDS3 char *vt, int hv,
+                    const LDS3 char *ktn, int hkn, const LDS3 char *vtn, int hvn,
+                    LDS3 char *kload, LDS3 char *vload, X8 (&vf0)[2], X8 (&kf0)[2], f32x16 &sc,
+                    f32x16 &sn, X8 (&pp)[2], X8 (&pc)[2]) __attribute__((always_inline)) {
+        constexpr bool LOADS = decltype(loads_tag)::value;
+        // Element mask of half tile h: visible iff 8(r/4) + r%4 <= lim.
+        const int lim = vis - 32 * h - 4 * g;
+        if (32 * h + 31 > (CAUSAL ? wrow0 : N - 1)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) > lim) sc[r] = -INFINITY;
+        }
+        // MFMA pair i: P V^T with V^T fragment (i / DB, i % DB), then K Q^T
+        // k-step i.  LDS reads in the order of use: pairs 2 .. KS-1 of this
+        // step, then pairs 0, 1 of the next.
+        X8 vf[KS], kf[KS];
+        vf[0] = vf0[0];
+        kf[0] = kf0[0];
+        vf[1] = vf0[1];
+        kf[1] = kf0[1];
+#pragma unroll
+        for (int i = 2; i < KS; ++i) read_pair(i, kt, hk, vt, hv, vf[i], kf[i]);
+        read_pair(0, ktn, hkn, vtn, hvn, vf0[0], kf0[0]);
+        read_pair(1, ktn, hkn, vtn, hvn, vf0[1], kf0[1]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            acc[i % DB] = Elem<E>::mfma(vf[i], pp[i / DB], acc[i % DB]);
+            sn = Elem<E>::mfma(kf[i], qop[i], sn);
+        }
+        float rs = exps(sc, mc_run, pc);
+        if constexpr (LOADS) {
+            const int t = h >> 1;
+            const E *kbase = Kh + (size_t)(t + 3) * kBc * kn;
+            const E *vbase = Vh + (size_t)(t + 2) * kBc * vn;
+            const int krows = min(kBc, kv_end - (t + 3) * kBc);
+            const int vrows = min(kBc, kv_end - (t + 2) * kBc);
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) {
+                tile_load<D, W, STRIDED>(kbase, krows, kn, kload, k_src, u, wave);
+                tile_load<D, W, STRIDED>(vbase, vrows, vn, vload, v_src, u, wave);
+            }
+        }
+        // Per pair: the three LDS reads of the pair two ahead (of the next
+        // step for the last two pairs), then each MFMA followed by its share
+        // of the softmax; the tile copies spread evenly.
+        constexpr int kValu = (56 + 2 * KS - 1) / (2 * KS);  // softmax VALU per MFMA
+        constexpr int kCopyEvery = KS / (2 * kLoads);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+            if (LOADS && i % kCopyEvery == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (__ballot(!(rs <= kSumMax<E>))) rs = rebase(sc, pc);
+        l_run += rs;
+    };
+
+    f32x16 sA, sB;
+    X8 pA[2], pB[2] = {X8{}, X8{}};
+    X8 vf0[2], kf0[2];
+    const std::integral_constant<bool, true> with_loads;
+    const std::integral_constant<bool, false> no_loads;
+
+    // Prologue: K(0), K(1), K(2), V(0), V(1) into LDS (tile step t copies
+    // K(t+3) and V(t+2)); scores of half tile 0; step 0 (whose P V^T adds
+    // zeros).
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            tile_load<D, W, STRIDED>(Kh + (size_t)i * kBc * kn, min(kBc, kv_end - i * kBc), kn, kb[i],
+                                     k_src, u, wave);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            tile_load<D, W, STRIDED>(Vh + (size_t)i * kBc * vn, min(kBc, kv_end - i * kBc), vn, vb[i],
+                                     v_src, u, wave);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    {
+        X8 kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const LDS3 X8 *>(kb[0] + k_rd[ks]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sA[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sA = Elem<E>::mfma(kf[ks], qop[ks], sA);
+    }
+    read_pair(0, kb[0], 1, vb[0], 0, vf0[0], kf0[0]);
+    read_pair(1, kb[0], 1, vb[0], 0, vf0[1], kf0[1]);
+    // Step 0 reads K half tile 1 (tile 0, half 1); step 1 reads K tile 1
+    // half 0 and V tile 0 half 0.
+    step(0, no_loads, kb[0], 1, vb[0], 0, kb[1], 0, vb[0], 0, kb[0], vb[0], vf0, kf0, sA, sB, pB, pA);
+
+    // Tile step t (buffers b = t mod 3): step 2t+1 reads K(t+1) half 0 and
+    // V(t) half 0, step 2t+2 their halves 1, and step 2t+3 (read ahead) K(t+2)
+    // half 0 and V(t+1) half 0.  A wave whose last visible half tile hlast
+    // has had its P V^T (step hlast+1) leaves the loop; for the rest of the
+    // workgroup's tiles it only issues its share of the copies and meets the
+    // barriers.
+    const int hlast = (min(kv_end - 1, vis_max) >> 5);
+    auto tile_step = [&](int t, int b) __attribute__((always_inline)) {
+        const int b1 = (b + 1) % 3, b2 = (b + 2) % 3;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        step(2 * t + 1, with_loads, kb[b1], 0, vb[b], 0, kb[b1], 1, vb[b], 1, kb[b], vb[b2], vf0,
+             kf0, sB, sA, pA, pB);
+        step(2 * t + 2, no_loads, kb[b1], 1, vb[b], 1, kb[b2], 0, vb[b1], 0, kb[b], vb[b2], vf0,
+             kf0, sA, sB, pB, pA);
+    };
+    int t = 0;
+    for (; t < n_tiles; t += 3) {
+        if (2 * t + 1 > hlast + 1) break;
+        tile_step(t, 0);
+        if (t + 1 >= n_tiles) {
+            t += 1;
+            break;
+        }
+        if (2 * t + 3 > hlast + 1) {
+            t += 1;
+            break;
+        }
+        tile_step(t + 1, 1);
+        if (t + 2 >= n_tiles) {
+            t += 2;
+            break;
+        }
+        if (2 * t + 5 > hlast + 1) {
+            t += 2;
+            break;
+        }
+        tile_step(t + 2, 2);
+    }
+    for (; t < n_tiles; ++t) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const E *kbase = Kh + (size_t)(t + 3) * kBc * kn;
+        const E *vbase = Vh + (size_t)(t + 2) * kBc * vn;
+        const int krows = min(kBc, kv_end - (t + 3) * kBc);
+        const int vrows = min(kBc, kv_end - (t + 2) * kBc);
+        const int b = t % 3;
+        LDS3 char *kload = b == 0 ? kb[0] : b == 1 ? kb[1] : kb[2];
+        LDS3 char *vload = b == 0 ? vb[2] : b == 1 ? vb[0] : vb[1];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            tile_load<D, W, STRIDED>(kbase, krows, kn, kload, k_src, u, wave);
+            tile_load<D, W, STRIDED>(vbase, vrows, vn, vload, v_src, u, wave);
+        }
+    }
+
+    // O = acc / l rounded to the element type; LSE = m * scale + ln(l).
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                         __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float inv = 1.f / l_tot;
+    if (qrow < N) {
+        E *orow = O + ooff + (size_t)qrow * on;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
+                *reinterpret_cast<X4 *>(orow + 32 * db + 8 * a + 4 * g) =
+                    __builtin_convertvector(x, X4);
+            }
+        if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
+    }
+}
+
+// Head dim 128 takes the software-pipelined kernel with 8-wave workgroups
+// (256 query rows); the other head dims the 128-row kernel.
+constexpr int kPipeWaves = 8;
+
 template <typename E, int D, bool CAUSAL, bool STRIDED>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                   int N, float scale, const FwdStrides &st, hipStream_t stream) {
-    const int nqt = (N + kBr - 1) / kBr;
-    const int blocks = B * H * nqt;
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads), 0, stream,
-                       static_cast<const E *>(q), static_cast<const E *>(k),
-                       static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, scale,
-                       scale_log2, st);
+    if constexpr (D == 128) {
+        constexpr int kRows = kPipeWaves * kRowsPerWave;
+        const int nqt = (N + kRows - 1) / kRows;
+        hipLaunchKernelGGL((fwd_pipe_kernel<E, D, CAUSAL, STRIDED, kPipeWaves>), dim3(B * H * nqt),
+                           dim3(64 * kPipeWaves), 0, stream, static_cast<const E *>(q),
+                           static_cast<const E *>(k), static_cast<const E *>(v),
+                           static_cast<E *>(o), lse, N, nqt, scale, scale_log2, st);
+    } else {
+        const int nqt = (N + kBr - 1) / kBr;
+        hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(B * H * nqt), dim3(kThreads),
+                           0, stream, static_cast<const E *>(q), static_cast<const E *>(k),
+                           static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, scale,
+                           scale_log2, st);
+    }
     return hipGetLastError();
 }
 
