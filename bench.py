@@ -201,7 +201,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _db_rows(d, q % counter)
-        fa_kib = [v for k, v in rows if "fwd_kernel" in k]
+        fa_kib = [v for k, v in rows if "fwd_kernel" in k or "fwd_pipe_kernel" in k]
         copy_kib = [v for k, v in rows if "copyBuffer" in k]
         if not fa_kib or len(copy_kib) != 1:
             raise SystemExit(f"{counter}: expected attention launches and one copy in {d}")
