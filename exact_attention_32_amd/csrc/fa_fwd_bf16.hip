@@ -585,9 +585,9 @@ constexpr int kPipeBufs = 3;
 // 8); at D = 64 and 128 the swizzle of a row depends on its index modulo 32
 // and 16 only, so the lane's gather offset `src` (that of load 0) serves
 // every load, with the descriptor's base moved to row u R and its size cut
-// to the rows that remain (the hardware range check, which covers the
-// vector offset only, then still turns every row at or past `rows` into
-// zeros; none remaining gives an empty range and a load of zeros only).
+// to the rows that remain (the hardware range check turns every row at or
+// past `rows` into zeros; none remaining gives an empty range and a load of
+// zeros only).
 template <int D, int W, bool STRIDED, typename E>
 __device__ __forceinline__ void tile_load(const E *base, int rows, int rs, LDS3 char *dst,
                                           uint32_t src, int u, int wave) {
