@@ -16,8 +16,12 @@
 //   LSE = ln sum_s e^(LSE_s),   O = sum_s e^(LSE_s - LSE) O_s.
 //
 // With a handful of queries the work is a matrix-vector product: about Nq
-// FLOP per byte of K and V, far below the MFMA balance point, so the kernel
-// is bound by HBM and runs on the vector ALUs.  Layout of a wave: groups of
+// FLOP per byte of K and V, far below the MFMA balance point, so the pass is
+// bound by HBM.  One or two queries run on the vector ALUs (the split kernel
+// below); from three queries on the VALU dot products no longer keep up with
+// HBM and the MFMA split kernel further down takes over (measured crossover
+// at B=2, H=32, Nk=8192, d=128: 49 vs 50 us at two queries, 57 vs 50 at
+// three).  Layout of a wave of the VALU kernel: groups of
 // G = d/8 lanes each hold one key row (16 bytes per lane), so one load
 // instruction reads 64/G consecutive rows (1 KiB, coalesced); the dot product
 // of a row with each query is summed over its group with DPP lane moves; every
@@ -31,13 +35,10 @@
 #include <cmath>
 
 #include "fa_internal.h"
+#include "fa_tiles.h"
 
 namespace fa {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -225,6 +226,238 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA split kernel, for more than kDecodeValuQueries queries.  The VALU
+// kernel above spends Nq DPP-reduced dot products per key row and stops
+// being bound by HBM at three queries; with the queries as one
+// 32-column block (columns past Nq are zero) the two products are MFMA
+// work, as in the forward kernels: S^T = K Q^T with K tiles read row-wise
+// from LDS, O^T += V^T P^T with V tiles read through the LDS transpose read,
+// the softmax in between (lazy exponent base, as in the forward pass).  Its
+// cost no longer grows with Nq.
+//
+// One wave per (batch*head, key chunk).  The chunk's keys go through 32-key
+// tiles of K and V copied global -> LDS by direct-to-LDS buffer loads into
+// three buffers private to the wave, two tiles ahead of the one being
+// multiplied; the wave waits for its own copies by vmcnt (no barrier), and
+// for its own reads of a buffer (lgkmcnt) before refilling it.  LDS layout
+// and read offsets: the shared swizzle of fa_tiles.h (conflict-free for
+// both read patterns).
+constexpr int kDecodeValuQueries = 2;  // at most this many queries: VALU kernel
+constexpr int kDecTile = 32;           // keys per LDS tile
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); a counter not waited for is set to its maximum.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Copy of the 32-key tile of K and V starting at key c0 (keys at or past
+// k1 read as zeros) into kd and vd: load u of the wave writes LDS bytes
+// u*1024 + 16*lane and fetches the global offset src[u] (row and swizzled
+// chunk).  (A function of its own: a buffer descriptor local to a lambda
+// makes the host pass drop the kernel's launch stub.)
+template <int D, int kLoads>
+__device__ __forceinline__ void decode_copy_tile(const __bf16 *Kh, const __bf16 *Vh, int c0, int k1,
+                                                 LDS3 char *kd, LDS3 char *vd,
+                                                 const uint32_t *src) {
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane(
+        (uint32_t)max(0, min(kDecTile, k1 - c0)) * (uint32_t)(D * 2));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(kd + u * 1024), 16, src[u], 0, 0,
+                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(vd + u * 1024), 16, src[u], 0, 0,
+                                                 0);
+    }
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
+                   const __bf16 *__restrict__ V, float *__restrict__ o_part,
+                   float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
+                   float scale_log2) {
+    constexpr int KS = D / 16;                 // k-steps of S^T = K Q^T
+    constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
+    constexpr int kRowsPerLoad = 64 / (D / 8);  // rows per 1 KiB load (4 or 8)
+    constexpr int kLoads = kDecTile / kRowsPerLoad;  // per operand and tile
+    constexpr int kTileBytes = kDecTile * D * 2;
+    __shared__ __attribute__((aligned(16))) __bf16 lk0[kDecTile * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lk1[kDecTile * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lk2[kDecTile * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lv0[kDecTile * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lv1[kDecTile * D];
+    __shared__ __attribute__((aligned(16))) __bf16 lv2[kDecTile * D];
+
+    const int lane = threadIdx.x;
+    const int g = lane >> 5;
+    const int j = lane & 31;  // query column of this lane
+    const int s = blockIdx.x % S;
+    const int bh = blockIdx.x / S;
+    const int k0 = s * chunk;
+    const int k1 = min(Nk, k0 + chunk);
+    const int n_tiles = (k1 - k0 + kDecTile - 1) / kDecTile;
+
+    // Q^T as the B operand: lane (g, j) holds query j (zero past Nq),
+    // columns 16ks + 8g .. +7.
+    bf16x8 qop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (j < Nq) x = load16(Q + ((size_t)bh * Nq + j) * D + 16 * ks + 8 * g);
+        qop[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+    // Query j sees keys up to vis (below the chunk's end; under the mask,
+    // keys <= Nk - Nq + j).
+    const int vis = CAUSAL ? min(k1 - 1, Nk - Nq + j) : k1 - 1;
+    const int vis_lo = CAUSAL ? min(k1 - 1, Nk - Nq) : k1 - 1;  // the least of the wave's
+
+    // Tile copies: load u fills LDS chunk positions u*64 + lane, i.e. row
+    // u*kRowsPerLoad + lane / (D/8), stored chunk lane % (D/8), and fetches the
+    // logical chunk the swizzle stores there.
+    uint32_t src[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int r = u * kRowsPerLoad + lane / (D / 8);
+        const int p = lane % (D / 8);
+        src[u] = (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
+    }
+    const __bf16 *Kh = K + (size_t)bh * Nk * D;
+    const __bf16 *Vh = V + (size_t)bh * Nk * D;
+    auto copy_tile = [&](int t, LDS3 char *kd, LDS3 char *vd) __attribute__((always_inline)) {
+        decode_copy_tile<D, kLoads>(Kh, Vh, k0 + t * kDecTile, k1, kd, vd, src);
+    };
+    static_assert(kLoads * 1024 == kTileBytes, "tile copy");
+
+    const uint32_t rd = row_read_offset<D>(lane);
+    uint32_t trd[2];
+    tr_read_offsets<D>(lane, trd);
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
+
+    // Probabilities of the tile's 32 keys against base mcx (scaled log2
+    // units) as P^T operands (keys 0-15, 16-31), and their half-wave sum.
+    auto exps = [&](const f32x16 &sc, float mcx, bf16x8 (&p)[2]) __attribute__((always_inline)) {
+        f32x8 lo, hi;
+        float ra = 0.f, rb = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], scale_log2, -mcx));
+            hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 8], scale_log2, -mcx));
+            ra += lo[r];
+            rb += hi[r];
+        }
+        p[0] = __builtin_convertvector(lo, bf16x8);
+        p[1] = __builtin_convertvector(hi, bf16x8);
+        return ra + rb;
+    };
+
+    // One tile: S^T, mask, softmax (lazy base: the base moves to the row
+    // maximum only when a half-row sum leaves (0, 2^32] or is not finite),
+    // O^T += V^T P^T; then the buffers are refilled with tile t + 3.
+    auto tile = [&](int t, LDS3 char *kt, LDS3 char *vt) __attribute__((always_inline)) {
+        // this tile's copies are the oldest outstanding ones
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kLoads));
+        f32x16 sc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(kt + row_read_at(rd, ks));
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qop[ks], sc, 0, 0, 0);
+        }
+        // Element r of sc is key c0 + 8(r/4) + 4g + r%4 of query j.
+        const int c0 = k0 + t * kDecTile;
+        if (c0 + kDecTile - 1 > vis_lo) {
+            const int lim = vis - c0 - 4 * g;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) > lim) sc[r] = -INFINITY;
+        }
+        bf16x8 pp[2];
+        float rs = exps(sc, mc_run, pp);
+        if (__ballot(!(rs <= 4294967296.f))) {
+            float mt = sc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                                 __float_as_uint(mt), false, false);
+                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const float m_new = fmaxf(m_run, mt);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha =
+                (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+            mc_run = m_use * scale_log2;
+            m_run = m_use;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            rs = exps(sc, mc_run, pp);
+        }
+        l_run += rs;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(vt, trd, tt, db), pp[tt],
+                                                                  acc[db], 0, 0, 0);
+        // every read of these buffers has completed before they are refilled
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        copy_tile(t + 3, kt, vt);
+    };
+
+    LDS3 char *const kb0 = (LDS3 char *)lk0;
+    LDS3 char *const kb1 = (LDS3 char *)lk1;
+    LDS3 char *const kb2 = (LDS3 char *)lk2;
+    LDS3 char *const vb0 = (LDS3 char *)lv0;
+    LDS3 char *const vb1 = (LDS3 char *)lv1;
+    LDS3 char *const vb2 = (LDS3 char *)lv2;
+    copy_tile(0, kb0, vb0);
+    copy_tile(1, kb1, vb1);
+    copy_tile(2, kb2, vb2);
+    // Whole rounds of three tiles (tiles past the chunk are empty copies and
+    // fully masked): every round issues the same copies in the same order,
+    // so the waits on the copies can be counted exactly.
+    for (int t = 0; t < n_tiles; t += 3) {
+        tile(t, kb0, vb0);
+        tile(t + 1, kb1, vb1);
+        tile(t + 2, kb2, vb2);
+    }
+    // No copy is left in flight when the wave ends.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                         __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (j < Nq) {
+        const size_t prow = ((size_t)bh * S + s) * Nq + j;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float *dst = o_part + prow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                *reinterpret_cast<float4 *>(dst + 32 * db + 8 * a + 4 * g) =
+                    make_float4(acc[db][4 * a] * inv, acc[db][4 * a + 1] * inv,
+                                acc[db][4 * a + 2] * inv, acc[db][4 * a + 3] * inv);
+        if (g == 0) lse_part[prow] = l_tot > 0.f ? m_run * scale + logf(l_tot) : -INFINITY;
+    }
+}
+
 // Merge kernel: one workgroup of 256 threads per output row (batch*head,
 // query) combines the row's S partial rows.  Every query sees key 0, so some
 // chunk has a finite LSE.
@@ -315,11 +548,17 @@ hipError_t launch_nq(const void *q, const void *k, const void *v, void *o, float
                      int H, int Nq, int Nk, int S, int chunk, float scale, float *o_part,
                      float *lse_part, hipStream_t stream) {
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL((decode_split_kernel<D, NQ, CAUSAL>), dim3(B * H * S),
-                       dim3(64 * kDecodeWaves<NQ>), 0, stream,
-                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-                       static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk, scale,
-                       scale_log2);
+    if constexpr (NQ > kDecodeValuQueries)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, CAUSAL>), dim3(B * H * S), dim3(64), 0, stream,
+                           static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
+                           static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk,
+                           scale, scale_log2);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, NQ, CAUSAL>), dim3(B * H * S),
+                           dim3(64 * kDecodeWaves<NQ>), 0, stream,
+                           static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
+                           static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk,
+                           scale, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(B * H * Nq), dim3(kMergeThreads), 0, stream,

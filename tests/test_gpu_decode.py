@@ -52,6 +52,14 @@ CASES = [
     (1, 1, 16, 16, 128, True, "normal", 0),
     (1, 2, 16, 2000, 64, False, "normal4", 0),
     (1, 2, 16, 3000, 128, True, "normal", 1000),
+    # more than four queries run on the MFMA split kernel: chunks of one to
+    # several 32-key tiles in rounds of three, and causal tail chunks that
+    # the first queries cannot see
+    (1, 2, 6, 130, 128, True, "normal", 3),
+    (1, 1, 16, 33, 64, True, "normal4", 0),
+    (2, 2, 12, 511, 128, False, "uniform", 2),
+    (1, 3, 7, 4096, 64, True, "normal", 0),
+    (1, 2, 9, 200, 64, True, "normal", 4),
 ]
 
 
