@@ -70,9 +70,17 @@ TRAFFIC_FILE = "profiles/fa_fwd_bf16_b2h32n8192d128_causal_traffic.txt"
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of the kernel sources' code: comments and whitespace are removed
+    first, so that editing a comment does not disown the committed counter
+    summaries."""
+    import re
+
     h = hashlib.sha256()
     for p in sources:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        text = open(os.path.join(ROOT, p), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
