@@ -294,7 +294,8 @@ def bench_decode(args) -> int:
             b.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    kernel_ms = sum(launch_ms) / len(launch_ms)
     ms_per_step = wall * 1e3 / args.steps
     gbs = w.bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
@@ -317,7 +318,9 @@ def bench_decode(args) -> int:
                    "tflops": round(w.flops / (kernel_ms * 1e-3) / 1e12, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "kernel_ms": round(kernel_ms, 4)},
+                     "traffic": None, "kernel_ms": round(kernel_ms, 4),
+                     "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
+                     "kernel_ms_min": round(launch_ms[0], 4)},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -523,7 +526,8 @@ def main() -> int:
             b.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    kernel_ms = sum(launch_ms) / len(launch_ms)
     ms_per_step = wall * 1e3 / args.steps
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -534,13 +538,17 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": read_traffic(w.name) if args.which == "fwd" else None,
-                "kernel_ms": round(kernel_ms, 4)}
+                "kernel_ms": round(kernel_ms, 4),
+                "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
+                "kernel_ms_min": round(launch_ms[0], 4)}
     if args.which == "kvouter":
         nbytes = kvouter_bytes(w)
         gbs = nbytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                    "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": nbytes}
+                    "kernel_ms": round(kernel_ms, 4),
+                    "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
+                    "kernel_ms_min": round(launch_ms[0], 4), "algorithmic_bytes": nbytes}
     if args.which == "bwd":
         metric = "attention bwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
     line = {
