@@ -8,7 +8,8 @@ three 64-key LDS buffers per operand in rotation, and lets a wave whose rows
 have seen all their keys leave the loop early.  The sequence lengths below
 sit on and around the boundaries of those pieces: half tiles (32), tiles
 (64), the three-buffer cycle (192), workgroups (256), and waves lying wholly
-past N in the last workgroup.
+past N in the last workgroup.  Causal head dim 64 with N >= 8192 runs the
+same kernel with 4-wave workgroups (test_d64_long_causal).
 """
 import numpy as np
 import pytest
@@ -57,6 +58,21 @@ def test_d128_grid_shapes(B, H, N, oracle_lib):
     """Workgroup counts that are (2 x 2 x 2 = 8) and are not (3, 15) a
     multiple of the XCD count, which changes the workgroup -> tile order."""
     _case(B, H, N, "uniform", True, "bf16", oracle_lib, seed=8000 + B * H * N)
+
+
+@pytest.mark.parametrize("N,dist,dtype", [(8200, "normal4", "bf16"), (8192, "normal", "f16"),
+                                          (9001, "uniform", "bf16")])
+def test_d64_long_causal(N, dist, dtype, oracle_lib):
+    """Causal head dim 64 with N >= 8192 runs the same pipelined kernel with
+    4-wave workgroups (128 rows); whole-tensor parity for one head, ragged
+    N included."""
+    w = inputs.Workload(f"d64_long_{N}_{dtype}_{dist}", 1, 1, N, 64, dtype, dist, True,
+                        seed=9000 + N)
+    print(f"case {w.name}", flush=True)
+    q, k, v = inputs.make_qkv(w)
+    o, lse = run_gpu(q, k, v, True, w.scale)
+    o_ref, lse_ref = oracle_lib.attention(q, k, v, w.scale, True)
+    check(o, lse, o_ref, lse_ref, dtype, w.name)
 
 
 def test_d128_strided_matches_dense():
