@@ -273,8 +273,12 @@ __device__ __forceinline__ void decode_copy_tile(const __bf16 *Kh, const __bf16 
     }
 }
 
+// (Two waves per SIMD at d = 64 keep the accumulators in VGPRs; at d = 128
+// the three tiles of LDS allow one workgroup per SIMD, and the compiler then
+// keeps them in AGPRs, costing only VALU slots this HBM-bound kernel has
+// spare.)
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
 decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, float *__restrict__ o_part,
                    float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
