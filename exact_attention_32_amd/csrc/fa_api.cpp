@@ -18,7 +18,7 @@ bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) 
 
 // Head dims of the forward kernels (fa_fwd, fa_fwd_f32, fa_fwd_ex) and of the
 // other paths (backward, decode, Algorithm 1 order).
-bool fwd_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+bool fwd_head_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 bool head_dim(int d) { return d == 64 || d == 128; }
 
 int validate(const void *q, const void *k, const void *v, const void *o, const void *lse,
@@ -266,7 +266,7 @@ const char *fa_strerror(int status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
         case FA_ERR_SHAPE: return "FA_ERR_SHAPE: need B, H, N >= 1, N <= 2^30 and B*H*N*d < 2^40";
-        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (forward: 32, 64, 96, 128; others: 64, 128)";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (forward: a multiple of 16 from 16 to 128; others: 64, 128)";
         case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
         case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";

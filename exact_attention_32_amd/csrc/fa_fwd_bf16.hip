@@ -1,7 +1,7 @@
 // fa_fwd_bf16.hip -- fused attention forward for gfx950: bf16 tensors (the
 // fa_fwd path) and, through the same template, fp16 tensors and strided
-// views (fa_fwd_ex); head dims 32, 64, 96 and 128; fp32 scores, softmax
-// statistics and accumulator.
+// views (fa_fwd_ex); head dims 16, 32, ..., 128 (multiples of 16); fp32
+// scores, softmax statistics and accumulator.
 //
 // What is computed: O = softmax(scale * Q K^T [+ causal mask]) V per
 // (batch, head), with the per-row log-sum-exp, as defined on the page
@@ -14,7 +14,7 @@
 // states both orders give the same result.
 //
 // Two kernels share the operand layouts, LDS swizzles, softmax and grid
-// mapping described here: fwd_kernel (head dims 32, 64, 96) and
+// mapping described here: fwd_kernel (the head dims other than 128) and
 // fwd_pipe_kernel (head dim 128), which reorders the work inside a wave
 // into a software pipeline and runs 8-wave workgroups; see its own comment
 // further down.
@@ -171,6 +171,11 @@ __device__ __forceinline__ int k_logical(int r, int p) {
 
 #define LDS3 __attribute__((address_space(3)))
 
+// Gather offset of a tile-copy lane with nothing to fetch: past the range of
+// every descriptor the copies build (at most 2^31 bytes), so the lane's 16
+// bytes arrive as zeros.
+constexpr uint32_t kNoChunk = 0xFFFFFFF0u;
+
 // Workgroup id -> (batch*head, query tile).  Consecutive ids go to
 // consecutive XCDs; when the grid divides evenly, XCD x receives the
 // contiguous range [x*W/8, (x+1)*W/8) of (head, tile) pairs.
@@ -207,7 +212,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // kernel's launch stub.)
 // Strided views (STRIDED): rows of K and V are kn and vn elements apart; the
 // descriptor then ends after the last valid row's d elements.
-template <int D, int kLoads, bool STRIDED, typename E>
+template <int DH, int kLoads, bool STRIDED, typename E>
 __device__ __forceinline__ void issue_tile_load(int i, const E *Kh, const E *Vh, int N, int c0,
                                                 LDS3 char *dk, LDS3 char *dv,
                                                 const uint32_t *k_src, const uint32_t *v_src,
@@ -215,22 +220,22 @@ __device__ __forceinline__ void issue_tile_load(int i, const E *Kh, const E *Vh,
     const int u = i >> 1;
     const int pos = (u * kWaves + wave) * 64 * 16;  // byte offset of this wave's 1 KiB
     if constexpr (!STRIDED) {
-        const uint32_t bytes = (uint32_t)min(kBc, N - c0) * (uint32_t)(D * 2);
+        const uint32_t bytes = (uint32_t)min(kBc, N - c0) * (uint32_t)(DH * 2);
         if ((i & 1) == 0) {
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * DH, bytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
         } else {
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * DH, bytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
         }
     } else {
         const uint32_t rows = (uint32_t)min(kBc, N - c0);
         if ((i & 1) == 0) {
-            const uint32_t bytes = (rows - 1) * (uint32_t)kn * 2u + (uint32_t)(D * 2);
+            const uint32_t bytes = (rows - 1) * (uint32_t)kn * 2u + (uint32_t)(DH * 2);
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * kn, bytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(dk + pos), 16, k_src[u], 0, 0, 0);
         } else {
-            const uint32_t bytes = (rows - 1) * (uint32_t)vn * 2u + (uint32_t)(D * 2);
+            const uint32_t bytes = (rows - 1) * (uint32_t)vn * 2u + (uint32_t)(DH * 2);
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * vn, bytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(dv + pos), 16, v_src[u], 0, 0, 0);
         }
@@ -243,14 +248,20 @@ struct FwdStrides {
     int qn, kn, vn, on, H;
 };
 
-template <typename E, int D, bool CAUSAL, bool STRIDED>
+template <typename E, int DH, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
            E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, float scale,
            float scale_log2, FwdStrides st) {
     typedef typename Elem<E>::x8 X8;
     typedef typename Elem<E>::x4 X4;
-    static_assert(D == 32 || D == 64 || D == 96 || D == 128, "head dim");
+    static_assert(DH % 16 == 0 && DH >= 16 && DH <= 128, "head dim");
+    // A head dim that is an odd multiple of 16 runs in the layout of the next
+    // multiple of 32 (D): S takes DH / 16 k-steps, the LDS tiles and the O^T
+    // blocks have D / 32 d-blocks, and the tile copies write zeros into the
+    // chunks at and past DH (their O^T rows are computed but never stored).
+    constexpr int D = (DH + 31) / 32 * 32;
+    constexpr int KS = DH / 16;                                 // k-steps of S^T = K Q^T
     constexpr int kChunksPerRow = D / 8;                        // 16-byte chunks
     constexpr int kLoads = kBc * kChunksPerRow / kThreads;     // per thread per tile
     // Two buffers per operand as four distinct objects: the tile loop is
@@ -284,8 +295,8 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
         vn = st.vn;
         on = st.on;
     } else {
-        qoff = koff = voff = ooff = (size_t)bh * (size_t)N * D;
-        qn = kn = vn = on = D;
+        qoff = koff = voff = ooff = (size_t)bh * (size_t)N * DH;
+        qn = kn = vn = on = DH;
     }
     const E *Qh = Q + qoff;
     const E *Kh = K + koff;
@@ -294,9 +305,9 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     const int qrow = wrow0 + j;
 
     // Q^T as the B operand: lane (g, j) holds query qrow, columns 16ks+8g..+7.
-    X8 qop[D / 16];
+    X8 qop[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
         qop[ks] = __builtin_bit_cast(X8, x);
@@ -310,25 +321,28 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     // fills position q = that base + l, i.e. row q / kChunksPerRow, stored
     // chunk q % kChunksPerRow, and must fetch the logical chunk that the
     // swizzle puts there.
+    // A position whose logical chunk lies at or past DH gets an offset past
+    // any descriptor's range, so the copy writes zeros there.
     uint32_t k_src[kLoads], v_src[kLoads];
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
         const int q = (u * kWaves + wave) * 64 + lane;
         const int r = q / kChunksPerRow;
         const int p = q % kChunksPerRow;
-        k_src[u] = (uint32_t)(r * kn * 2 + (k_logical<D>(r, p) << 4));
-        v_src[u] = (uint32_t)(r * vn * 2 + ((p ^ v_swz<D>(r)) << 4));
+        const int ck = k_logical<D>(r, p), cv = p ^ v_swz<D>(r);
+        k_src[u] = (DH == D || ck < DH / 8) ? (uint32_t)(r * kn * 2 + (ck << 4)) : kNoChunk;
+        v_src[u] = (DH == D || cv < DH / 8) ? (uint32_t)(r * vn * 2 + (cv << 4)) : kNoChunk;
     }
-    // The 2 kLoads tile loads are spread evenly over the D/16 k-steps of S.
-    constexpr int kLoadStride = (D / 16) / (2 * kLoads);
-    static_assert(kLoadStride >= 1 && kLoadStride * 2 * kLoads == D / 16, "load spacing");
+    // The 2 kLoads tile loads are spread evenly over the KS k-steps of S:
+    // k-step ks issues loads [ks L / KS, (ks + 1) L / KS), L = 2 kLoads.
+    constexpr int kTileLoads = 2 * kLoads;
 
     // MFMA operand read offsets (bytes within a tile).
     // K (A operand of S^T = K Q^T): lane (g, j) reads row 32kb + j, logical
     // chunk 2ks + g.
-    uint32_t k_rd[D / 16];
+    uint32_t k_rd[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
         k_rd[ks] = (uint32_t)(j * D * 2 + (k_stored<D>(j, 2 * ks + g) << 4));
     // V^T (A operand of O^T += V^T P^T) through the 16-lane transpose read:
     // in group G = lane/16 (m0 = 16*(G&1), g = G>>1), lane i of the group reads
@@ -367,8 +381,8 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
         const int c0 = t * kBc;
         const bool prefetch = t + 1 < n_tiles;
         auto load = [&](int i) __attribute__((always_inline)) {
-            issue_tile_load<D, kLoads, STRIDED>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src, wave,
-                                                kn, vn);
+            issue_tile_load<DH, kLoads, STRIDED>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src,
+                                                 wave, kn, vn);
         };
 
         // A wave whose rows all precede this tile has nothing to add.
@@ -387,9 +401,9 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
             // All K fragments of the tile are requested before the first MFMA,
             // so the LDS latency is paid once per tile, not once per k-step.
-            X8 kf[D / 16][kBc / 32];
+            X8 kf[KS][kBc / 32];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
                     kf[ks][kb] = *reinterpret_cast<const LDS3 X8 *>(
@@ -402,11 +416,14 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
             __builtin_amdgcn_s_setprio(1);
             // The next tile's loads go out one per k-step, between the MFMAs.
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
                     s[kb] = Elem<E>::mfma(kf[ks][kb], qop[ks], s[kb]);
-                if (prefetch && ks % kLoadStride == 0) load(ks / kLoadStride);
+                if (prefetch) {
+#pragma unroll
+                    for (int i = ks * kTileLoads / KS; i < (ks + 1) * kTileLoads / KS; ++i) load(i);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
 
@@ -512,7 +529,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
 
 #pragma unroll
     for (int i = 0; i < 2 * kLoads; ++i)
-        issue_tile_load<D, kLoads, STRIDED>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave, kn, vn);
+        issue_tile_load<DH, kLoads, STRIDED>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave, kn, vn);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < n_tiles; t += 2) {
@@ -534,11 +551,12 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
+                const int col = 32 * db + 8 * a + 4 * g;
+                if (DH % 32 != 0 && col >= DH) continue;
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
-                *reinterpret_cast<X4 *>(orow + 32 * db + 8 * a + 4 * g) =
-                    __builtin_convertvector(x, X4);
+                *reinterpret_cast<X4 *>(orow + col) = __builtin_convertvector(x, X4);
             }
         if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
     }
@@ -970,7 +988,7 @@ fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
 // takes it with 4-wave workgroups (two per CU); there it measured 3-4 %
 // faster than the 128-row kernel, which stays ahead on shorter sequences
 // (fewer, longer workgroups start and drain less evenly).  The other head
-// dims take the 128-row kernel.
+// dims (every multiple of 16 up to 128) take the 128-row kernel.
 constexpr int kPipeWaves = 8;
 constexpr int kPipeWaves64 = 4;
 constexpr int kPipeMinN64 = 8192;
@@ -1019,12 +1037,19 @@ template <typename E, bool STRIDED>
 hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                     int N, int d, float scale, bool causal, const FwdStrides &st,
                     hipStream_t stream) {
+#define FA_FWD_CASE(DH) \
+    case DH: return launch_c<E, DH, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream)
     switch (d) {
-        case 32: return launch_c<E, 32, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
-        case 64: return launch_c<E, 64, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
-        case 96: return launch_c<E, 96, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
+        FA_FWD_CASE(16);
+        FA_FWD_CASE(32);
+        FA_FWD_CASE(48);
+        FA_FWD_CASE(64);
+        FA_FWD_CASE(80);
+        FA_FWD_CASE(96);
+        FA_FWD_CASE(112);
         default: return launch_c<E, 128, STRIDED>(q, k, v, o, lse, B, H, N, scale, causal, st, stream);
     }
+#undef FA_FWD_CASE
 }
 
 }  // namespace

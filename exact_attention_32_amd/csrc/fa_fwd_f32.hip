@@ -145,9 +145,13 @@ hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float 
                           int B, int H, int N, int d, float scale, bool causal,
                           hipStream_t stream) {
     switch (d) {
+        case 16: return launch_c<16>(q, k, v, o, lse, B, H, N, scale, causal, stream);
         case 32: return launch_c<32>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        case 48: return launch_c<48>(q, k, v, o, lse, B, H, N, scale, causal, stream);
         case 64: return launch_c<64>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        case 80: return launch_c<80>(q, k, v, o, lse, B, H, N, scale, causal, stream);
         case 96: return launch_c<96>(q, k, v, o, lse, B, H, N, scale, causal, stream);
+        case 112: return launch_c<112>(q, k, v, o, lse, B, H, N, scale, causal, stream);
         default: return launch_c<128>(q, k, v, o, lse, B, H, N, scale, causal, stream);
     }
 }

@@ -34,8 +34,8 @@
  *            page, section 4, last steps of Algorithm 1; this library returns
  *            the single number m*scale + ln(l) instead.)
  * Shapes:    B, H, N >= 1; N <= 2^30; B*H*N*d < 2^40; the head dim d is
- *            32, 64, 96 or 128 for the forward entry points (fa_fwd,
- *            fa_fwd_f32, fa_fwd_ex) and 64 or 128 for the others.
+ *            a multiple of 16 from 16 to 128 for the forward entry points
+ *            (fa_fwd, fa_fwd_f32, fa_fwd_ex) and 64 or 128 for the others.
  * scale:     finite and > 0 (usually 1/sqrt(d)).
  * causal:    0 = no mask, any other value = top-left causal mask.
  * Errors:    all argument checks run before anything is enqueued; a failed

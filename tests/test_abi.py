@@ -74,9 +74,9 @@ def test_validation_codes(fn, lib):
     assert _call(fn, N=0) == fa.FA_ERR_SHAPE
     assert _call(fn, N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
     assert _call(fn, B=1 << 16, H=1 << 10, N=1 << 10) == fa.FA_ERR_SHAPE  # 2^42 elements
-    for d in (0, 16, 48, 80, 127, 256):
+    for d in (0, 8, 24, 72, 127, 144, 256):
         assert _call(fn, d=d) == fa.FA_ERR_HEADDIM
-    for d in (32, 96):   # forward head dims beyond 64 and 128: fail later, on the scale
+    for d in (16, 32, 48, 80, 96, 112):   # every multiple of 16 up to 128: fails later, on the scale
         assert _call(fn, d=d, scale=0.0) == fa.FA_ERR_SCALE
     for s in (0.0, -0.125, float("inf"), float("nan")):
         assert _call(fn, scale=s) == fa.FA_ERR_SCALE

@@ -172,7 +172,7 @@ def test_error_codes_on_device():
     with pytest.raises(fa.FAError) as e:
         fa.forward(q, k, v, out=q)
     assert e.value.code == fa.FA_ERR_ALIAS
-    q3 = torch.zeros(1, 1, 64, 80, dtype=torch.bfloat16, device="cuda")
+    q3 = torch.zeros(1, 1, 64, 72, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.FAError) as e:
         fa.forward(q3, q3.clone(), q3.clone())
     assert e.value.code == fa.FA_ERR_HEADDIM

@@ -15,14 +15,14 @@ RNG = np.random.default_rng(20260)
 DISTS = ["normal", "normal4", "uniform"]
 
 
-def _cfgs(n, dims, dtypes):
+def _cfgs(n, dims, dtypes, rng=RNG, seed0=7000):
     out = []
     for i in range(n):
-        out.append(dict(B=int(RNG.integers(1, 3)), H=int(RNG.integers(1, 4)),
-                        N=int(RNG.integers(1, 700)), d=int(RNG.choice(dims)),
-                        dtype=str(RNG.choice(dtypes)), dist=str(RNG.choice(DISTS)),
-                        causal=bool(RNG.integers(0, 2)), layout=str(RNG.choice(["dense", "bnhd"])),
-                        seed=7000 + i))
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+                        N=int(rng.integers(1, 700)), d=int(rng.choice(dims)),
+                        dtype=str(rng.choice(dtypes)), dist=str(rng.choice(DISTS)),
+                        causal=bool(rng.integers(0, 2)), layout=str(rng.choice(["dense", "bnhd"])),
+                        seed=seed0 + i))
     return out
 
 
@@ -32,6 +32,10 @@ DEC = [dict(B=int(RNG.integers(1, 3)), H=int(RNG.integers(1, 4)), Nq=int(RNG.int
             Nk=int(RNG.integers(16, 3000)), d=int(RNG.choice([64, 128])),
             causal=bool(RNG.integers(0, 2)), dist=str(RNG.choice(DISTS)),
             splits=int(RNG.choice([0, 1, 3, 17])), seed=8000 + i) for i in range(10)]
+# Head dims that are odd multiples of 16, from a generator of their own (the
+# draws above stay as they were).
+FWD_ODD = _cfgs(8, [16, 48, 80, 112], ["bf16", "f16"], rng=np.random.default_rng(20261),
+                seed0=7500)
 
 
 def _err(o, ref):
@@ -39,7 +43,7 @@ def _err(o, ref):
     return float(np.abs(o - ref).max()), float(np.linalg.norm(o - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-@pytest.mark.parametrize("c", FWD, ids=lambda c: f"N{c['N']}d{c['d']}{c['dtype']}{c['layout']}c{int(c['causal'])}")
+@pytest.mark.parametrize("c", FWD + FWD_ODD, ids=lambda c: f"N{c['N']}d{c['d']}{c['dtype']}{c['layout']}c{int(c['causal'])}")
 def test_random_forward(c, oracle_lib):
     w = inputs.Workload("rf", c["B"], c["H"], c["N"], c["d"], c["dtype"], c["dist"], c["causal"],
                         seed=c["seed"])
