@@ -98,6 +98,30 @@ def make_qkv(w: Workload, device="cpu"):
     return tuple(t.to(dt).contiguous().to(device) for t in (q, k, v))
 
 
+def make_qkv_device(w: Workload, device):
+    """(q, k, v) with make_qkv's recipe (distribution; Q, then K, then V),
+    drawn on ``device`` from a torch generator of that device seeded with the
+    workload's seed, one batch entry at a time.  For tensors too large to
+    draw on the host in reasonable time; the numbers differ from make_qkv's."""
+    g = torch.Generator(device).manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    dt = torch_dtype(w.dtype)
+    big = w.dist == "normal4"
+    out = []
+    for which in range(3):
+        t = torch.empty(shape, dtype=dt, device=device)
+        for b in range(w.B):
+            if w.dist == "uniform":
+                x = 2.0 * torch.rand(shape[1:], generator=g, device=device, dtype=torch.float32) - 1.0
+            else:
+                x = torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32)
+                if big and which < 2:
+                    x = 4.0 * x
+            t[b].copy_(x)
+        out.append(t)
+    return tuple(out)
+
+
 @dataclasses.dataclass(frozen=True)
 class DecodeWorkload:
     """Nq queries (the newest positions) over Nk keys of each (batch, head)."""
