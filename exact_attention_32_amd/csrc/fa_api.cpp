@@ -16,8 +16,8 @@ bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) 
     return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
-// Head dims of the forward kernels (fa_fwd, fa_fwd_f32, fa_fwd_ex) and of the
-// other paths (backward, decode, Algorithm 1 order).
+// Head dims of the forward and backward kernels (fa_fwd, fa_fwd_f32,
+// fa_fwd_ex, fa_bwd) and of the other paths (decode, Algorithm 1 order).
 bool fwd_head_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 bool head_dim(int d) { return d == 64 || d == 128; }
 
@@ -50,7 +50,7 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
                  const void *delta, int B, int H, int N, int d, float scale) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!fwd_head_dim(d)) return FA_ERR_HEADDIM;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -266,7 +266,7 @@ const char *fa_strerror(int status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
         case FA_ERR_SHAPE: return "FA_ERR_SHAPE: need B, H, N >= 1, N <= 2^30 and B*H*N*d < 2^40";
-        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (forward: a multiple of 16 from 16 to 128; others: 64, 128)";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (forward and backward: a multiple of 16 from 16 to 128; decode, Algorithm 1 order: 64, 128)";
         case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
         case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";

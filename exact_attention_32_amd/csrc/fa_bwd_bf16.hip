@@ -52,6 +52,13 @@ namespace {
 // d = 128); there its two 32-query halves run as a loop, not unrolled, which
 // keeps their live ranges apart (a few registers still go to scratch, which
 // measured faster than one wave per SIMD).
+//
+// A head dim DH that is not 64 or 128 runs in the tile layout of the next of
+// the two (D): S and dP take DH/16 k-steps, the tiles and the dQ, dK, dV
+// accumulators have D/32 d-blocks, and only the first DH columns are
+// stored; the tile columns at and past DH feed only the unstored rows.
+template <int DH>
+constexpr int kLayout = DH <= 64 ? 64 : 128;
 template <int D>
 constexpr int kDqWaves = 2;
 template <int D>
@@ -59,13 +66,16 @@ constexpr int kDkdvWaves = 2;
 template <int D>
 constexpr int kHalfUnroll = D == 128 ? 1 : 2;
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>, kDqWaves<D>)))
+template <int DH, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kDqWaves<kLayout<DH>>, kDqWaves<kLayout<DH>>)))
 bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
               const __bf16 *__restrict__ V, const __bf16 *__restrict__ O,
               const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
               float *__restrict__ Delta, __bf16 *__restrict__ dQ, int N, int ntiles,
               float scale, float scale_log2) {
+    constexpr int D = kLayout<DH>;
+    constexpr int KS = DH / 16;  // k-steps of S^T and dP^T
     __shared__ __attribute__((aligned(16))) __bf16 lds_k0[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_k1[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_v0[kInner * D];
@@ -80,7 +90,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     int bh, qt;
     map_block(blockIdx.x, gridDim.x, ntiles, CAUSAL, bh, qt);
     const int r0 = qt * kOuter;
-    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const size_t hoff = (size_t)bh * (size_t)N * DH;
     const __bf16 *Kh = K + hoff;
     const __bf16 *Vh = V + hoff;
     const int wrow0 = r0 + wave * kRowsPerWave;
@@ -90,13 +100,13 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // Q^T and dO^T as B operands: lane (g, j) holds columns 16ks+8g..+7 of
     // its query row.  D_i = dO_i . O_i from the same columns, then summed
     // over the two half-waves.
-    bf16x8 qop[D / 16], doop[D / 16];
+    bf16x8 qop[KS], doop[KS];
     float dpart = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
         if (valid) {
-            const size_t e = hoff + (size_t)qrow * D + 16 * ks + 8 * g;
+            const size_t e = hoff + (size_t)qrow * DH + 16 * ks + 8 * g;
             xq = load16(Q + e);
             xd = load16(dO + e);
             xo = load16(O + e);
@@ -119,7 +129,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int kv_end = CAUSAL ? min(N, r0 + kOuter) : N;
     const int n_tiles = (kv_end + kInner - 1) / kInner;
 
-    const uint32_t src = tile_src_offset<D>(wave, lane);
+    const uint32_t src = tile_src_offset<D, DH>(wave, lane);
     const uint32_t rd = row_read_offset<D>(lane);
     uint32_t trd[2];
     tr_read_offsets<D>(lane, trd);
@@ -138,8 +148,8 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk, LDS3 char *nv) {
         const int c0 = t * kInner;
         if (t + 1 < n_tiles) {
-            load_tile<D>(Kh, N, c0 + kInner, nk, src, wave);
-            load_tile<D>(Vh, N, c0 + kInner, nv, src, wave);
+            load_tile<D, DH>(Kh, N, c0 + kInner, nk, src, wave);
+            load_tile<D, DH>(Vh, N, c0 + kInner, nv, src, wave);
         }
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
         if (active) {
@@ -150,7 +160,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < kInner / 32; ++kb) {
                     const uint32_t a = row_read_at(rd, ks) + kb * 32 * D * 2;
@@ -197,15 +207,15 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         __syncthreads();
     };
 
-    load_tile<D>(Kh, N, 0, k0, src, wave);
-    load_tile<D>(Vh, N, 0, v0, src, wave);
+    load_tile<D, DH>(Kh, N, 0, k0, src, wave);
+    load_tile<D, DH>(Vh, N, 0, v0, src, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < n_tiles; t += 2) {
         step(t, k0, v0, k1, v1);
         if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
     }
-    if (valid) store_rows<D>(dQ + hoff + (size_t)qrow * D, acc, scale, g);
+    if (valid) store_rows<D, DH>(dQ + hoff + (size_t)qrow * DH, acc, scale, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -213,14 +223,16 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 // keys k0 + 32w .. +31 (lane (g, j) holds key j of the wave).  Query tiles
 // of 64 rows stream through LDS together with their LSE and D values.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int DH, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>, kDkdvWaves<D>)))
+__attribute__((amdgpu_waves_per_eu(kDkdvWaves<kLayout<DH>>, kDkdvWaves<kLayout<DH>>)))
 bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
                 const float *__restrict__ LSE, const float *__restrict__ Delta,
                 __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, int ntiles,
                 float scale, float scale_log2) {
+    constexpr int D = kLayout<DH>;
+    constexpr int KS = DH / 16;  // k-steps of S and dP
     __shared__ __attribute__((aligned(16))) __bf16 lds_q0[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_q1[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_o0[kInner * D];
@@ -240,7 +252,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // are issued first (no reversal).
     map_block(blockIdx.x, gridDim.x, ntiles, false, bh, kt);
     const int k0 = kt * kOuter;
-    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const size_t hoff = (size_t)bh * (size_t)N * DH;
     const __bf16 *Qh = Q + hoff;
     const __bf16 *dOh = dO + hoff;
     const float *LSEh = LSE + (size_t)bh * N;
@@ -250,12 +262,12 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const bool valid = key < N;
 
     // K^T and V^T as B operands: lane (g, j) holds columns 16ks+8g..+7 of its key.
-    bf16x8 kop[D / 16], vop[D / 16];
+    bf16x8 kop[KS], vop[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
         if (valid) {
-            const size_t e = hoff + (size_t)key * D + 16 * ks + 8 * g;
+            const size_t e = hoff + (size_t)key * DH + 16 * ks + 8 * g;
             xk = load16(K + e);
             xv = load16(V + e);
         }
@@ -267,7 +279,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int t_begin = CAUSAL ? k0 / kInner : 0;
     const int n_tiles = (N + kInner - 1) / kInner;
 
-    const uint32_t src = tile_src_offset<D>(wave, lane);
+    const uint32_t src = tile_src_offset<D, DH>(wave, lane);
     const uint32_t rd = row_read_offset<D>(lane);
     uint32_t trd[2];
     tr_read_offsets<D>(lane, trd);
@@ -286,8 +298,8 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // Rows c0 .. c0+63 of Q and dO, and their LSE and D (waves 0 and 1 copy
     // those, one 4-byte direct-to-LDS load each; entries past N read as 0).
     auto load_all = [&](int c0, LDS3 char *dq_, LDS3 char *do_, LDS3 float *st) {
-        load_tile<D>(Qh, N, c0, dq_, src, wave);
-        load_tile<D>(dOh, N, c0, do_, src, wave);
+        load_tile<D, DH>(Qh, N, c0, dq_, src, wave);
+        load_tile<D, DH>(dOh, N, c0, do_, src, wave);
         if (wave < 2) load_vec(wave == 0 ? LSEh : Dh, N, c0, st + wave * kInner, lane);
     };
 
@@ -304,7 +316,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int qb = 0; qb < kInner / 32; ++qb) {
                 f32x16 s = {}, dp = {};
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
+                for (int ks = 0; ks < KS; ++ks) {
                     const uint32_t a = row_read_at(rd, ks) + qb * 32 * D * 2;
                     const bf16x8 qf = *reinterpret_cast<const LDS3 bf16x8 *>(qt_ + a);
                     const bf16x8 of = *reinterpret_cast<const LDS3 bf16x8 *>(ot_ + a);
@@ -366,8 +378,8 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         }
     }
     if (valid) {
-        store_rows<D>(dK + hoff + (size_t)key * D, acck, scale, g);
-        store_rows<D>(dV + hoff + (size_t)key * D, accv, 1.f, g);
+        store_rows<D, DH>(dK + hoff + (size_t)key * DH, acck, scale, g);
+        store_rows<D, DH>(dV + hoff + (size_t)key * DH, accv, 1.f, g);
     }
 }
 
@@ -398,11 +410,27 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            const void *dout, const float *lse, void *dq, void *dk, void *dv,
                            float *delta, int B, int H, int N, int d, float scale, bool causal,
                            hipStream_t stream) {
-    if (d == 64)
-        return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream)
-                      : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream);
-    return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream)
-                  : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, stream);
+#define FA_BWD_CASE(DH)                                                                          \
+    case DH:                                                                                     \
+        return causal ? launch<DH, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale,  \
+                                         stream)                                                 \
+                      : launch<DH, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, \
+                                          stream)
+    switch (d) {
+        FA_BWD_CASE(16);
+        FA_BWD_CASE(32);
+        FA_BWD_CASE(48);
+        FA_BWD_CASE(64);
+        FA_BWD_CASE(80);
+        FA_BWD_CASE(96);
+        FA_BWD_CASE(112);
+        default:
+            return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
+                                              scale, stream)
+                          : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
+                                               scale, stream);
+    }
+#undef FA_BWD_CASE
 }
 
 }  // namespace fa

@@ -57,22 +57,28 @@ __device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse
     if (reverse) tile = ntiles - 1 - tile;
 }
 
-// Direct-to-LDS copy of one kInner-row tile of a [N, D] bf16 matrix (rows r0
-// .. r0 + kInner - 1; rows >= N read as zeros) into `dst`, swizzled: lane l of
-// load u of wave w writes chunk position q = (u*kWaves + w)*64 + l, and
-// fetches the logical chunk that the swizzle stores there.  Load u is 4 KiB
-// (16 or 32 rows) after load 0 on both sides and leaves the row's swizzle
-// term unchanged, so one lane offset `src` (load 0) serves every load.
-template <int D>
+// Direct-to-LDS copy of one kInner-row tile of a [N, DH] bf16 matrix (rows
+// r0 .. r0 + kInner - 1; rows >= N read as zeros) into `dst`, a tile of
+// kInner rows of D >= DH columns, swizzled: lane l of load u of wave w
+// writes chunk position q = (u*kWaves + w)*64 + l, and fetches the logical
+// chunk that the swizzle stores there.  Load u covers the rows 16 (D = 128)
+// or 32 (D = 64) after load 0's, which leaves the row's swizzle term
+// unchanged, so one lane offset `src` (load 0) serves every load, moved by
+// that many rows of DH elements.  With DH < D the columns at and past DH
+// receive the next row's leading elements (or zeros past the tile's last
+// row): callers use them only for output rows they never store.
+template <int D, int DH = D>
 __device__ __forceinline__ void load_tile(const __bf16 *mat, int N, int r0, LDS3 char *dst,
                                           uint32_t src, int wave) {
+    static_assert(DH <= D && DH % 16 == 0, "row length");
     constexpr int kLoads = kInner * (D / 8) / kThreads;
-    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - r0)) * (uint32_t)(D * 2);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat + (size_t)r0 * D, bytes);
+    constexpr int kRowsPerLoad = kWaves * 1024 / (D * 2);
+    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - r0)) * (uint32_t)(DH * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat + (size_t)r0 * DH, bytes);
 #pragma unroll
     for (int u = 0; u < kLoads; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)(dst + (u * kWaves + wave) * 1024),
-                                                 16, src, u * kWaves * 1024, 0, 0);
+                                                 16, src, u * kRowsPerLoad * DH * 2, 0, 0);
 }
 
 // Direct-to-LDS copy of vec[c0 .. c0 + 63] (fp32; entries at or past N read
@@ -85,12 +91,12 @@ __device__ __forceinline__ void load_vec(const float *vec, int N, int c0, LDS3 f
 }
 
 // Lane source offset of load_tile's first load (see there).
-template <int D>
+template <int D, int DH = D>
 __device__ __forceinline__ uint32_t tile_src_offset(int wave, int lane) {
     const int q = wave * 64 + lane;
     const int r = q / (D / 8);
     const int p = q % (D / 8);
-    return (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
+    return (uint32_t)(r * DH * 2 + ((p ^ swz<D>(r)) << 4));
 }
 
 // Byte offset (within a tile) of the 128-bit operand read of k-step ks: lane
@@ -140,13 +146,15 @@ __device__ __forceinline__ u32x4 load16(const __bf16 *p) {
 }
 
 // Store a [D x 32] accumulator block set (lane (g, j) holds row `row` of the
-// result, columns 32db + 8a + 4g + e in acc[db][4a + e]) times `mul` as bf16.
-template <int D>
+// result, columns 32db + 8a + 4g + e in acc[db][4a + e]) times `mul` as bf16;
+// only the first DH columns are stored.
+template <int D, int DH = D>
 __device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, float mul, int g) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            if (DH < D && 32 * db + 8 * a + 4 * g >= DH) continue;
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * mul;

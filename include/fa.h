@@ -35,7 +35,8 @@
  *            the single number m*scale + ln(l) instead.)
  * Shapes:    B, H, N >= 1; N <= 2^30; B*H*N*d < 2^40; the head dim d is
  *            a multiple of 16 from 16 to 128 for the forward entry points
- *            (fa_fwd, fa_fwd_f32, fa_fwd_ex) and 64 or 128 for the others.
+ *            (fa_fwd, fa_fwd_f32, fa_fwd_ex) and fa_bwd, and 64 or 128 for
+ *            fa_decode and fa_fwd_kv_outer.
  * scale:     finite and > 0 (usually 1/sqrt(d)).
  * causal:    0 = no mask, any other value = top-left causal mask.
  * Errors:    all argument checks run before anything is enqueued; a failed

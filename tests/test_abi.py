@@ -120,8 +120,10 @@ def test_bwd_validation_codes(lib):
         assert _bwd(**{name: 0}) == fa.FA_ERR_NULL, name
     assert _bwd(B=0) == fa.FA_ERR_SHAPE
     assert _bwd(N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
-    assert _bwd(d=96) == fa.FA_ERR_HEADDIM       # the backward pass takes 64 and 128
-    assert _bwd(d=32) == fa.FA_ERR_HEADDIM
+    for d in (0, 8, 72, 144):                    # multiples of 16 up to 128 only
+        assert _bwd(d=d) == fa.FA_ERR_HEADDIM
+    for d in (16, 32, 96, 112):                  # accepted: fails later, on the scale
+        assert _bwd(d=d, scale=0.0) == fa.FA_ERR_SCALE
     assert _bwd(scale=float("nan")) == fa.FA_ERR_SCALE
     assert _bwd(scale=0.0) == fa.FA_ERR_SCALE
     assert _bwd(dk=BDK + 8) == fa.FA_ERR_ALIGN

@@ -9,6 +9,7 @@ masks, ragged and one-row sequences, fp16, fp32 (the vector-ALU kernel),
 [B, N, H, d] views, reads past the last row, and writes: nothing outside O
 changes.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -102,3 +103,97 @@ def test_head_dim_rejected():
         with pytest.raises(fa.FAError) as e:
             fa.forward(q, q.clone(), q.clone())
         assert e.value.code == fa.FA_ERR_HEADDIM
+
+
+# --- backward at the head dims other than 64 and 128 --------------------------
+# The backward kernels run DH < 64 in the 64-column layout and 64 < DH < 128
+# in the 128-column one (S and dP over DH/16 k-steps; dQ, dK, dV stored for
+# the first DH columns only).  Gates and delta check of test_gpu_backward,
+# whose derivation assumes rows of many keys: with two keys, dP - delta is
+# P1 (dP0 - dP1) and cancels, so the 2^-9 rounding of O inside delta alone
+# moves dQ and dK by up to 1e-2 relative at any head dim (measured at N = 2
+# for d = 32, 64, 128: 1.7e-3 .. 1.1e-2).  N = 33 is the shortest ragged
+# length here; one key has its own test.
+BWD_DIMS = [16, 32, 48, 80, 96, 112]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [33, 77, 300])
+@pytest.mark.parametrize("d", BWD_DIMS)
+def test_backward(d, N, causal, oracle_lib):
+    from .test_gpu_backward import check_delta, check_grad, run_bwd
+
+    w = inputs.Workload(f"bwd_d{d}_{N}_{int(causal)}", 1, 2, N, d, "bf16", "normal", causal,
+                        seed=17000 + 10 * d + N)
+    print(f"case {w.name}", flush=True)
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    dq, dk, dv, o, delta = run_bwd(q, k, v, dout, causal, w.scale)
+    refs = oracle_lib.attention_backward(q, k, v, dout, w.scale, causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        check_grad(g, r, f"{w.name} {name}")
+    check_delta(delta, dout, o, w.name)
+
+
+@pytest.mark.parametrize("d", BWD_DIMS)
+def test_backward_single_key(d):
+    """N = 1: the one probability is 1, so dV = dO exactly and dQ = dK = 0 up
+    to the rounding of dP - delta (two fp32 dot products of the same terms,
+    summed in different orders); the relative gates of the other cases have
+    no scale here (the exact gradients are 0)."""
+    from .test_gpu_backward import run_bwd
+
+    w = inputs.Workload(f"bwd_d{d}_n1", 2, 3, 1, d, "bf16", "normal", False, seed=17500 + d)
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    dq, dk, dv, _, _ = run_bwd(q, k, v, dout, False, w.scale)
+    assert np.array_equal(dv, dout.float().double().numpy())
+    bound = 1e-5 * float(np.abs(dout.float().numpy()).max() * np.abs(v.float().numpy()).max()) * d
+    assert float(np.abs(dq).max()) <= bound and float(np.abs(dk).max()) <= bound
+
+
+@pytest.mark.parametrize("d", [48, 112])
+def test_backward_large_logits(d, oracle_lib):
+    from .test_gpu_backward import check_grad, run_bwd
+
+    w = inputs.Workload(f"bwd_d{d}_big", 2, 1, 257, d, "bf16", "normal4", True, seed=18000 + d)
+    q, k, v = inputs.make_qkv(w)
+    dout = inputs.make_dout(w)
+    dq, dk, dv, _, _ = run_bwd(q, k, v, dout, True, w.scale)
+    refs = oracle_lib.attention_backward(q, k, v, dout, w.scale, True)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        check_grad(g, r, f"{w.name} {name}", big_logits=True)
+
+
+@pytest.mark.parametrize("d", BWD_DIMS)
+def test_backward_guard_and_bounds(d):
+    """NaN after every input and around each gradient: the gradients are
+    bit-equal to those of plain allocations and nothing outside them is
+    written (no store past d or past the last row)."""
+    w = inputs.Workload(f"bwd_d{d}_guard", 1, 2, 1000, d, "bf16", "normal", True, seed=19000 + d)
+    q, k, v = (t.cuda() for t in inputs.make_qkv(w))
+    dout = inputs.make_dout(w).cuda()
+    o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+    r1 = fa.backward(q, k, v, o, lse, dout, causal=True, scale=w.scale)
+    pad = 1 << 14
+
+    def nan_backed(t):
+        buf = torch.full((t.numel() + pad,), float("nan"), dtype=t.dtype, device="cuda")
+        buf[: t.numel()].copy_(t.reshape(-1))
+        return buf[: t.numel()].view(t.shape), buf
+
+    qn, kn, vn, on, ln, dn = (nan_backed(t)[0] for t in (q, k, v, o, lse, dout))
+    outs = []
+    for t in r1[:3]:
+        buf = torch.full((t.numel() + 2 * pad,), float("nan"), dtype=t.dtype, device="cuda")
+        outs.append((buf[pad: pad + t.numel()].view(t.shape), buf))
+    delta = torch.empty_like(lse)
+    rc = fa.fa_bwd(qn, kn, vn, on, dn, ln, outs[0][0], outs[1][0], outs[2][0], delta, 1, 2, 1000,
+                   d, w.scale, True, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert rc == fa.FA_OK
+    for a, (b, buf) in zip(r1[:3], outs):
+        n = a.numel()
+        assert torch.equal(a, b) and bool(torch.isfinite(b.float()).all())
+        assert bool(torch.isnan(buf[:pad].float()).all()) and bool(torch.isnan(buf[pad + n:].float()).all())
+    print(f"backward guard d={d} ok", flush=True)

@@ -36,6 +36,8 @@ DEC = [dict(B=int(RNG.integers(1, 3)), H=int(RNG.integers(1, 4)), Nq=int(RNG.int
 # draws above stay as they were).
 FWD_ODD = _cfgs(8, [16, 48, 80, 112], ["bf16", "f16"], rng=np.random.default_rng(20261),
                 seed0=7500)
+BWD_ODD = _cfgs(6, [16, 32, 48, 80, 96, 112], ["bf16"], rng=np.random.default_rng(20262),
+                seed0=7600)
 
 
 def _err(o, ref):
@@ -61,7 +63,7 @@ def test_random_forward(c, oracle_lib):
     assert ma <= ga and rel <= gr and le <= 1e-3
 
 
-@pytest.mark.parametrize("c", BWD, ids=lambda c: f"N{c['N']}d{c['d']}c{int(c['causal'])}")
+@pytest.mark.parametrize("c", BWD + BWD_ODD, ids=lambda c: f"N{c['N']}d{c['d']}c{int(c['causal'])}")
 def test_random_backward(c, oracle_lib):
     w = inputs.Workload("rb", c["B"], c["H"], c["N"], c["d"], "bf16", c["dist"], c["causal"],
                         seed=c["seed"])
