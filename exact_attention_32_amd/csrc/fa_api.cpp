@@ -16,16 +16,14 @@ bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) 
     return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
-// Head dims of the forward and backward kernels (fa_fwd, fa_fwd_f32,
-// fa_fwd_ex, fa_bwd) and of the other paths (decode, Algorithm 1 order).
-bool fwd_head_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
-bool head_dim(int d) { return d == 64 || d == 128; }
+// Head dims of every entry point: multiples of 16 from 16 to 128.
+bool head_dim_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 
 int validate(const void *q, const void *k, const void *v, const void *o, const void *lse,
-             int B, int H, int N, int d, float scale, uint64_t elem_bytes, bool fwd_dims) {
+             int B, int H, int N, int d, float scale, uint64_t elem_bytes) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
-    if (!(fwd_dims ? fwd_head_dim(d) : head_dim(d))) return FA_ERR_HEADDIM;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
     // B*H*N*d < 2^40, evaluated without overflow (N*d < 2^38, B*H < 2^62).
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
@@ -50,7 +48,7 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
                  const void *delta, int B, int H, int N, int d, float scale) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
-    if (!fwd_head_dim(d)) return FA_ERR_HEADDIM;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -75,7 +73,7 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
 bool decode_shape_ok(int B, int H, int Nq, int Nk, int d) {
     if (B < 1 || H < 1 || Nq < 1 || Nq > fa::kDecodeMaxQueries || Nk < Nq || Nk > (1 << 30))
         return false;
-    if (d != 64 && d != 128) return false;
+    if (!head_dim_ok(d)) return false;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     return bh <= ((1ull << 40) - 1) / ((uint64_t)Nk * (uint64_t)d);
 }
@@ -98,9 +96,9 @@ uint64_t kvouter_workspace(int B, int H, int N, int d, uint64_t *l_off, uint64_t
     return o_bytes + 2 * v_bytes;
 }
 
-bool fwd_shape_ok(int B, int H, int N, int d, bool fwd_dims) {
+bool shape_ok(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return false;
-    if (!(fwd_dims ? fwd_head_dim(d) : head_dim(d))) return false;
+    if (!head_dim_ok(d)) return false;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     return bh <= ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d);
 }
@@ -133,7 +131,7 @@ extern "C" {
 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
            int N, int d, float scale, int causal, hipStream_t stream) {
-    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, true);
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2);
     if (rc != FA_OK) return rc;
     const hipError_t e =
         fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream);
@@ -142,7 +140,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B,
                int H, int N, int d, float scale, int causal, hipStream_t stream) {
-    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 4, true);
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 4);
     if (rc != FA_OK) return rc;
     const hipError_t e =
         fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream);
@@ -163,9 +161,9 @@ int fa_fwd_ex(int dtype, const void *q, const void *k, const void *v, void *o, f
               int B, int H, int N, int d, float scale, int causal, const int64_t *strides,
               hipStream_t stream) {
     if (!q || !k || !v || !o || !lse || !strides) return FA_ERR_NULL;
-    if (!fwd_shape_ok(B, H, N, d, true)) {
+    if (!shape_ok(B, H, N, d)) {
         if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
-        if (!fwd_head_dim(d)) return FA_ERR_HEADDIM;
+        if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
         return FA_ERR_SHAPE;
     }
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
@@ -196,14 +194,14 @@ int fa_fwd_ex(int dtype, const void *q, const void *k, const void *v, void *o, f
 }
 
 size_t fa_fwd_kv_outer_workspace_size(int B, int H, int N, int d) {
-    if (!fwd_shape_ok(B, H, N, d, false)) return 0;
+    if (!shape_ok(B, H, N, d)) return 0;
     return (size_t)kvouter_workspace(B, H, N, d, nullptr, nullptr);
 }
 
 int fa_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                     int H, int N, int d, float scale, int causal, void *workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, false);
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2);
     if (rc != FA_OK) return rc;
     uint64_t l_off = 0, m_off = 0;
     const uint64_t need = kvouter_workspace(B, H, N, d, &l_off, &m_off);
@@ -233,7 +231,7 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nq > fa::kDecodeMaxQueries || Nk < Nq || Nk > (1 << 30))
         return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
     if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
     const int S = fa::decode_num_splits(B, H, Nk, num_splits);
@@ -266,7 +264,7 @@ const char *fa_strerror(int status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
         case FA_ERR_SHAPE: return "FA_ERR_SHAPE: need B, H, N >= 1, N <= 2^30 and B*H*N*d < 2^40";
-        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (forward and backward: a multiple of 16 from 16 to 128; decode, Algorithm 1 order: 64, 128)";
+        case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (need a multiple of 16 from 16 to 128)";
         case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
         case FA_ERR_HIP: return "FA_ERR_HIP: the kernel launch failed";

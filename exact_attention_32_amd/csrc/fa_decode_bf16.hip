@@ -91,12 +91,20 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float *acc, floa
 template <int NQ>
 constexpr int kDecodeWaves = (NQ + 3) / 4;
 
-template <int D, int NQ, bool CAUSAL>
+// A head dim DH other than 64 and 128 runs in the layout of the next of the
+// two (D): lanes whose 8 columns lie at or past DH hold zeros and load and
+// store nothing; rows are DH elements apart in memory and in the partial
+// outputs.
+template <int DH>
+constexpr int kDecLayout = DH <= 64 ? 64 : 128;
+
+template <int DH, int NQ, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kDecodeWaves<NQ>)
 decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     const __bf16 *__restrict__ V, float *__restrict__ o_part,
                     float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
                     float scale_log2) {
+    constexpr int D = kDecLayout<DH>;
     constexpr int G = D / 8;       // lanes per key row
     constexpr int RPW = 64 / G;    // rows per load instruction
     constexpr int NQW = NQ < 4 ? NQ : 4;  // queries per wave
@@ -111,14 +119,15 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int bh = blockIdx.x / S;
     const int k0 = s * chunk;
     const int k1 = min(Nk, k0 + chunk);
+    const bool has_cols = DH == D || col * 8 < DH;  // this lane's columns exist
 
     // This lane's 8 columns of every query of the wave, widened to fp32.
     float qf[NQW][8];
 #pragma unroll
     for (int qi = 0; qi < NQW; ++qi) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (qbase + qi < Nq)
-            w = *reinterpret_cast<const u32x4 *>(Q + ((size_t)bh * Nq + qbase + qi) * D + col * 8);
+        if (qbase + qi < Nq && has_cols)
+            w = *reinterpret_cast<const u32x4 *>(Q + ((size_t)bh * Nq + qbase + qi) * DH + col * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             qf[qi][2 * e] = bf16_lo(w[e]);
@@ -134,17 +143,17 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
     }
 
-    const __bf16 *Kh = K + (size_t)bh * Nk * D + col * 8;
-    const __bf16 *Vh = V + (size_t)bh * Nk * D + col * 8;
+    const __bf16 *Kh = K + (size_t)bh * Nk * DH + col * 8;
+    const __bf16 *Vh = V + (size_t)bh * Nk * DH + col * 8;
     for (int base = k0; base < k1; base += BLK) {
         u32x4 kr[ROUNDS], vr[ROUNDS];
 #pragma unroll
         for (int r = 0; r < ROUNDS; ++r) {
             const int j = base + r * RPW + grp;
             kr[r] = vr[r] = u32x4{0u, 0u, 0u, 0u};
-            if (j < k1) {
-                kr[r] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)j * D);
-                vr[r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)j * D);
+            if (j < k1 && has_cols) {
+                kr[r] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)j * DH);
+                vr[r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)j * DH);
             }
         }
         // Scores of the block's rows (identical in all G lanes of a group).
@@ -215,12 +224,14 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             if (qbase + qi >= Nq) break;
             const size_t prow = ((size_t)bh * S + s) * Nq + qbase + qi;
             const float inv = l[qi] > 0.f ? 1.f / l[qi] : 0.f;
-            float *dst = o_part + prow * D + col * 8;
+            float *dst = o_part + prow * DH + col * 8;
+            if (has_cols) {
 #pragma unroll
-            for (int e = 0; e < 8; e += 4)
-                *reinterpret_cast<float4 *>(dst + e) =
-                    make_float4(acc[qi][e] * inv, acc[qi][e + 1] * inv, acc[qi][e + 2] * inv,
-                                acc[qi][e + 3] * inv);
+                for (int e = 0; e < 8; e += 4)
+                    *reinterpret_cast<float4 *>(dst + e) =
+                        make_float4(acc[qi][e] * inv, acc[qi][e + 1] * inv, acc[qi][e + 2] * inv,
+                                    acc[qi][e + 3] * inv);
+            }
             if (col == 0) lse_part[prow] = l[qi] > 0.f ? m[qi] * scale + logf(l[qi]) : -INFINITY;
         }
     }
@@ -256,14 +267,14 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // u*1024 + 16*lane and fetches the global offset src[u] (row and swizzled
 // chunk).  (A function of its own: a buffer descriptor local to a lambda
 // makes the host pass drop the kernel's launch stub.)
-template <int D, int kLoads>
+template <int DH, int kLoads>
 __device__ __forceinline__ void decode_copy_tile(const __bf16 *Kh, const __bf16 *Vh, int c0, int k1,
                                                  LDS3 char *kd, LDS3 char *vd,
                                                  const uint32_t *src) {
     const uint32_t bytes = __builtin_amdgcn_readfirstlane(
-        (uint32_t)max(0, min(kDecTile, k1 - c0)) * (uint32_t)(D * 2));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * D, bytes);
+        (uint32_t)max(0, min(kDecTile, k1 - c0)) * (uint32_t)(DH * 2));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * DH, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * DH, bytes);
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(kd + u * 1024), 16, src[u], 0, 0,
@@ -277,13 +288,20 @@ __device__ __forceinline__ void decode_copy_tile(const __bf16 *Kh, const __bf16 
 // the three tiles of LDS allow one workgroup per SIMD, and the compiler then
 // keeps them in AGPRs, costing only VALU slots this HBM-bound kernel has
 // spare.)
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+// A head dim DH other than 64 and 128 runs in the tile layout of the next of
+// the two (D): S^T takes DH/16 k-steps, O^T has D/32 d-blocks, the tile rows
+// are gathered at the DH row stride (the columns at and past DH hold the
+// next row's leading elements, or zeros past the tile, and feed only the
+// O^T rows at and past DH), and the first DH columns are stored.
+template <int DH, bool CAUSAL>
+__global__ void __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(kDecLayout<DH> == 64 ? 2 : 1)))
 decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, float *__restrict__ o_part,
                    float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
                    float scale_log2) {
-    constexpr int KS = D / 16;                 // k-steps of S^T = K Q^T
+    constexpr int D = kDecLayout<DH>;
+    constexpr int KS = DH / 16;                // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
     constexpr int kRowsPerLoad = 64 / (D / 8);  // rows per 1 KiB load (4 or 8)
     constexpr int kLoads = kDecTile / kRowsPerLoad;  // per operand and tile
@@ -310,7 +328,7 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (j < Nq) x = load16(Q + ((size_t)bh * Nq + j) * D + 16 * ks + 8 * g);
+        if (j < Nq) x = load16(Q + ((size_t)bh * Nq + j) * DH + 16 * ks + 8 * g);
         qop[ks] = __builtin_bit_cast(bf16x8, x);
     }
     // Query j sees keys up to vis (below the chunk's end; under the mask,
@@ -326,12 +344,12 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     for (int u = 0; u < kLoads; ++u) {
         const int r = u * kRowsPerLoad + lane / (D / 8);
         const int p = lane % (D / 8);
-        src[u] = (uint32_t)(r * D * 2 + ((p ^ swz<D>(r)) << 4));
+        src[u] = (uint32_t)(r * DH * 2 + ((p ^ swz<D>(r)) << 4));
     }
-    const __bf16 *Kh = K + (size_t)bh * Nk * D;
-    const __bf16 *Vh = V + (size_t)bh * Nk * D;
+    const __bf16 *Kh = K + (size_t)bh * Nk * DH;
+    const __bf16 *Vh = V + (size_t)bh * Nk * DH;
     auto copy_tile = [&](int t, LDS3 char *kd, LDS3 char *vd) __attribute__((always_inline)) {
-        decode_copy_tile<D, kLoads>(Kh, Vh, k0 + t * kDecTile, k1, kd, vd, src);
+        decode_copy_tile<DH, kLoads>(Kh, Vh, k0 + t * kDecTile, k1, kd, vd, src);
     };
     static_assert(kLoads * 1024 == kTileBytes, "tile copy");
 
@@ -450,14 +468,17 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     if (j < Nq) {
         const size_t prow = ((size_t)bh * S + s) * Nq + j;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *dst = o_part + prow * D;
+        float *dst = o_part + prow * DH;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                *reinterpret_cast<float4 *>(dst + 32 * db + 8 * a + 4 * g) =
+            for (int a = 0; a < 4; ++a) {
+                const int col = 32 * db + 8 * a + 4 * g;
+                if (DH < D && col >= DH) continue;
+                *reinterpret_cast<float4 *>(dst + col) =
                     make_float4(acc[db][4 * a] * inv, acc[db][4 * a + 1] * inv,
                                 acc[db][4 * a + 2] * inv, acc[db][4 * a + 3] * inv);
+            }
         if (g == 0) lse_part[prow] = l_tot > 0.f ? m_run * scale + logf(l_tot) : -INFINITY;
     }
 }
@@ -491,10 +512,13 @@ __device__ __forceinline__ void merge_pair(float &m, float &l, float mo, float l
     m = mn;
 }
 
-template <int D>
+template <int DH>
 __global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ lse_part,
                     __bf16 *__restrict__ O, float *__restrict__ LSE, int Nq, int S) {
+    // Threads are laid out over D >= DH columns (a divisor of the workgroup
+    // size); those of the columns at and past DH add nothing.
+    constexpr int D = DH <= 64 ? 64 : 128;
     constexpr int kSlices = kMergeThreads / D;
     __shared__ float wts[kMergeChunk];
     __shared__ float red_m[kMergeThreads / 64], red_l[kMergeThreads / 64];
@@ -527,9 +551,9 @@ decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ 
         for (int s = t; s < n; s += kMergeThreads)
             wts[s] = __builtin_amdgcn_exp2f((lp[(size_t)(s0 + s) * Nq] - lse) * kLog2e);
         __syncthreads();
-        const float *op = o_part + (((size_t)bh * S + s0) * Nq + qi) * D + c;
-        const size_t stride = (size_t)Nq * D;
-        int s = slice;
+        const float *op = o_part + (((size_t)bh * S + s0) * Nq + qi) * DH + c;
+        const size_t stride = (size_t)Nq * DH;
+        int s = c < DH ? slice : n;
         for (; s + kSlices < n; s += 2 * kSlices) {
             acc0 = __builtin_fmaf(wts[s], op[(size_t)s * stride], acc0);
             acc1 = __builtin_fmaf(wts[s + kSlices], op[(size_t)(s + kSlices) * stride], acc1);
@@ -538,11 +562,11 @@ decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ 
     }
     part[t] = acc0 + acc1;
     __syncthreads();
-    if (slice == 0) {
+    if (slice == 0 && c < DH) {
         float o = part[c];
 #pragma unroll
         for (int k = 1; k < kSlices; ++k) o += part[k * D + c];
-        O[(size_t)row * D + c] = (__bf16)o;
+        O[(size_t)row * DH + c] = (__bf16)o;
         if (c == 0) LSE[row] = lse;
     }
 }
@@ -610,15 +634,27 @@ hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void 
                               int S, float *o_part, float *lse_part, hipStream_t stream) {
     const int chunk = decode_chunk(Nk, S);
     S = (Nk + chunk - 1) / chunk;  // no empty chunk
-    if (d == 64)
-        return causal ? launch_d<64, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
-                                           lse_part, stream)
-                      : launch_d<64, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
-                                            lse_part, stream);
-    return causal ? launch_d<128, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
-                                        lse_part, stream)
-                  : launch_d<128, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,
-                                         lse_part, stream);
+#define FA_DEC_CASE(DH)                                                                          \
+    case DH:                                                                                     \
+        return causal ? launch_d<DH, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,  \
+                                           lse_part, stream)                                     \
+                      : launch_d<DH, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale,         \
+                                            o_part, lse_part, stream)
+    switch (d) {
+        FA_DEC_CASE(16);
+        FA_DEC_CASE(32);
+        FA_DEC_CASE(48);
+        FA_DEC_CASE(64);
+        FA_DEC_CASE(80);
+        FA_DEC_CASE(96);
+        FA_DEC_CASE(112);
+        default:
+            return causal ? launch_d<128, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale,
+                                                o_part, lse_part, stream)
+                          : launch_d<128, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale,
+                                                 o_part, lse_part, stream);
+    }
+#undef FA_DEC_CASE
 }
 
 }  // namespace fa

@@ -35,13 +35,19 @@
 namespace fa {
 namespace {
 
-template <int D, bool CAUSAL>
+// A head dim DH other than 64 and 128 runs in the tile layout of the next of
+// the two (D): S^T takes DH/16 k-steps, the tiles and O^T have D/32
+// d-blocks, and only the first DH columns of O are read, kept and stored
+// (the tile columns at and past DH feed only the O^T rows past DH).
+template <int DH, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     const __bf16 *__restrict__ V, float *__restrict__ Ows,
                     float *__restrict__ Lws, float *__restrict__ Mws, __bf16 *__restrict__ O,
                     float *__restrict__ LSE, int N, int nqb, int j, int i0, float scale,
                     float scale_log2) {
+    constexpr int D = DH <= 64 ? 64 : 128;
+    constexpr int KS = DH / 16;
     __shared__ __attribute__((aligned(16))) __bf16 lds_k[kInner * D];
     __shared__ __attribute__((aligned(16))) __bf16 lds_v[kInner * D];
 
@@ -54,23 +60,23 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int bh = blockIdx.x / per_head;
     const int i = i0 + blockIdx.x % per_head;
     const int r0 = i * kOuter;
-    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const size_t hoff = (size_t)bh * (size_t)N * DH;
     const int wrow0 = r0 + wave * kRowsPerWave;
     const int qrow = wrow0 + jq;
     const bool valid = qrow < N;
     const int c0 = j * kInner;
 
     // line 6: K_j, V_j to on-chip memory
-    const uint32_t src = tile_src_offset<D>(wave, lane);
-    load_tile<D>(K + hoff, N, c0, (LDS3 char *)lds_k, src, wave);
-    load_tile<D>(V + hoff, N, c0, (LDS3 char *)lds_v, src, wave);
+    const uint32_t src = tile_src_offset<D, DH>(wave, lane);
+    load_tile<D, DH>(K + hoff, N, c0, (LDS3 char *)lds_k, src, wave);
+    load_tile<D, DH>(V + hoff, N, c0, (LDS3 char *)lds_v, src, wave);
 
     // line 8: Q_i (as the B operand of S^T = K Q^T) and the row state
-    bf16x8 qop[D / 16];
+    bf16x8 qop[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (valid) x = load16(Q + hoff + (size_t)qrow * D + 16 * ks + 8 * g);
+        if (valid) x = load16(Q + hoff + (size_t)qrow * DH + 16 * ks + 8 * g);
         qop[ks] = __builtin_bit_cast(bf16x8, x);
     }
     // The first key block a row block meets is j = 0 (every row sees key 0).
@@ -80,7 +86,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const bool last = j == j_last;
     float m_i = -INFINITY, l_i = 0.f;
     f32x16 o_i[D / 32];
-    float *orow = Ows + hoff + (size_t)qrow * D;
+    float *orow = Ows + hoff + (size_t)qrow * DH;
     if (!first && valid) {
         m_i = Mws[(size_t)bh * N + qrow];
         l_i = Lws[(size_t)bh * N + qrow];
@@ -88,7 +94,9 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(orow + 32 * db + 8 * a + 4 * g);
+                const int col = 32 * db + 8 * a + 4 * g;
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                if (DH == D || col < DH) x = *reinterpret_cast<const f32x4 *>(orow + col);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o_i[db][4 * a + e] = x[e];
             }
@@ -109,7 +117,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
     const uint32_t rd = row_read_offset<D>(lane);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < kInner / 32; ++kb) {
             const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(
@@ -188,7 +196,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     if (!valid) return;
     if (last) {
         // the algorithm's result: O and LSE = m*scale + ln(l)
-        store_rows<D>(O + hoff + (size_t)qrow * D, o_i, 1.f, g);
+        store_rows<D, DH>(O + hoff + (size_t)qrow * DH, o_i, 1.f, g);
         if (g == 0) LSE[(size_t)bh * N + qrow] = m_new * scale + logf(l_new);
     } else {
         // line 13: the state back to device memory
@@ -196,10 +204,12 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
+                const int col = 32 * db + 8 * a + 4 * g;
+                if (DH < D && col >= DH) continue;
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = o_i[db][4 * a + e];
-                *reinterpret_cast<f32x4 *>(orow + 32 * db + 8 * a + 4 * g) = x;
+                *reinterpret_cast<f32x4 *>(orow + col) = x;
             }
         if (g == 0) {
             Mws[(size_t)bh * N + qrow] = m_new;
@@ -234,11 +244,24 @@ hipError_t launch_fwd_kvouter_bf16(const void *q, const void *k, const void *v, 
                                    float *lse, int B, int H, int N, int d, float scale,
                                    bool causal, float *ows, float *lws, float *mws,
                                    hipStream_t stream) {
-    if (d == 64)
-        return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream)
-                      : launch<64, false>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream);
-    return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream)
-                  : launch<128, false>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream);
+#define FA_KVO_CASE(DH)                                                                          \
+    case DH:                                                                                     \
+        return causal ? launch<DH, true>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream)    \
+                      : launch<DH, false>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream)
+    switch (d) {
+        FA_KVO_CASE(16);
+        FA_KVO_CASE(32);
+        FA_KVO_CASE(48);
+        FA_KVO_CASE(64);
+        FA_KVO_CASE(80);
+        FA_KVO_CASE(96);
+        FA_KVO_CASE(112);
+        default:
+            return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws, stream)
+                          : launch<128, false>(q, k, v, o, lse, B, H, N, scale, ows, lws, mws,
+                                               stream);
+    }
+#undef FA_KVO_CASE
 }
 
 }  // namespace fa

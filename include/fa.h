@@ -34,9 +34,7 @@
  *            page, section 4, last steps of Algorithm 1; this library returns
  *            the single number m*scale + ln(l) instead.)
  * Shapes:    B, H, N >= 1; N <= 2^30; B*H*N*d < 2^40; the head dim d is
- *            a multiple of 16 from 16 to 128 for the forward entry points
- *            (fa_fwd, fa_fwd_f32, fa_fwd_ex) and fa_bwd, and 64 or 128 for
- *            fa_decode and fa_fwd_kv_outer.
+ *            a multiple of 16 from 16 to 128 for every entry point.
  * scale:     finite and > 0 (usually 1/sqrt(d)).
  * causal:    0 = no mask, any other value = top-left causal mask.
  * Errors:    all argument checks run before anything is enqueued; a failed
@@ -157,8 +155,9 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
  *               bytes for the fp32 partials; its contents on return are
  *               unspecified; it must not overlap any other argument
  * Scores, statistics and sums are fp32.  Shapes: B, H >= 1, 1 <= Nq <= 16,
- * Nq <= Nk <= 2^30, d is 64 or 128, B*H*Nk*d < 2^40.  Two kernels are enqueued
- * on `stream`.  Errors as for fa_fwd, plus FA_ERR_WORKSPACE.
+ * Nq <= Nk <= 2^30, d a multiple of 16 up to 128, B*H*Nk*d < 2^40.  Two
+ * kernels are enqueued on `stream`.  Errors as for fa_fwd, plus
+ * FA_ERR_WORKSPACE.
  */
 int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int Nq, int Nk, int d, float scale, int causal,

@@ -143,8 +143,9 @@ def test_decode_workspace_size(lib):
     assert ws(1, 1, 1, 100, 64, 1) < ws(1, 1, 1, 100, 64, 2)
     assert ws(1, 1, 1, 4096, 128, 10 ** 6) == ws(1, 1, 1, 4096, 128, 64)   # capped at Nk/64
     for bad in ((0, 1, 1, 100, 64, 0), (1, 1, 0, 100, 64, 0), (1, 1, 17, 100, 64, 0),
-                (1, 1, 8, 7, 64, 0), (1, 1, 1, 100, 96, 0)):
+                (1, 1, 8, 7, 64, 0), (1, 1, 1, 100, 72, 0), (1, 1, 1, 100, 144, 0)):
         assert ws(*bad) == 0, bad
+    assert ws(1, 1, 1, 100, 96, 1) >= 96 * 4 + 4   # every multiple of 16 up to 128
 
 
 def test_decode_validation_codes(lib):
@@ -159,7 +160,8 @@ def test_decode_validation_codes(lib):
     assert call(Nq=0) == fa.FA_ERR_SHAPE
     assert call(Nq=17) == fa.FA_ERR_SHAPE
     assert call(Nq=8, Nk=7) == fa.FA_ERR_SHAPE
-    assert call(d=80) == fa.FA_ERR_HEADDIM
+    assert call(d=72) == fa.FA_ERR_HEADDIM
+    assert call(d=80, scale=-1.0) == fa.FA_ERR_SCALE   # 80 is accepted
     assert call(scale=-1.0) == fa.FA_ERR_SCALE
     assert call(ws=0) == fa.FA_ERR_WORKSPACE
     assert call(wsb=16) == fa.FA_ERR_WORKSPACE
@@ -173,7 +175,8 @@ def test_kv_outer_validation_and_size(lib):
     ws = fa.fa_fwd_kv_outer_workspace_size
     assert ws(1, 1, 100, 64) >= 100 * 64 * 4 + 2 * 100 * 4
     assert ws(2, 3, 100, 128) > ws(1, 3, 100, 128)
-    assert ws(1, 1, 0, 64) == 0 and ws(1, 1, 10, 80) == 0
+    assert ws(1, 1, 0, 64) == 0 and ws(1, 1, 10, 72) == 0
+    assert ws(1, 1, 10, 80) >= 10 * 80 * 4 + 2 * 10 * 4
     W = BASE + 7 * GAP
 
     def call(**kw):

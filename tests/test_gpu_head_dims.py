@@ -1,5 +1,8 @@
-"""Forward pass at the head dims that are odd multiples of 16 (16, 48, 80,
-112), against the fp64 oracle with the gates of test_gpu_parity.
+"""Every entry point at the head dims other than 64 and 128, against the
+fp64 oracle.  Forward: the odd multiples of 16 (16, 48, 80, 112; 32 and 96
+have layouts of their own and are in test_gpu_forward_ex), gates of
+test_gpu_parity.  Backward, decode and the Algorithm 1 order: 16, 32, 48,
+80, 96, 112 (further down).
 
 These run the 128-row kernel in the layout of the next multiple of 32: S
 takes d/16 k-steps, the LDS tiles and the output blocks are 32 columns wider
@@ -197,3 +200,69 @@ def test_backward_guard_and_bounds(d):
         assert torch.equal(a, b) and bool(torch.isfinite(b.float()).all())
         assert bool(torch.isnan(buf[:pad].float()).all()) and bool(torch.isnan(buf[pad + n:].float()).all())
     print(f"backward guard d={d} ok", flush=True)
+
+
+# --- decode and the Algorithm 1 order at the head dims other than 64 and 128
+# Both run DH in the layout of the next of 64 and 128 (decode: lanes of the
+# columns at and past DH hold zeros in the vector-ALU kernel; the MFMA kernel
+# and the Algorithm 1 kernel as the backward's tiles).  Gates of
+# test_gpu_decode and test_gpu_kvouter (the forward's bf16 gates).
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq", [1, 2, 5, 16])
+@pytest.mark.parametrize("d", BWD_DIMS)
+def test_decode(d, nq, causal, oracle_lib):
+    from .test_gpu_decode import check as dcheck, run_decode
+
+    w = inputs.DecodeWorkload(f"dec_d{d}_nq{nq}_{int(causal)}", 2, 2, nq, 333, d, "normal", causal,
+                              seed=20000 + 10 * d + nq)
+    print(f"case {w.name}", flush=True)
+    q, k, v = inputs.make_decode_qkv(w)
+    for splits in (0, 3):
+        o, lse = run_decode(q, k, v, causal, w.scale, splits)
+        o_ref, lse_ref = oracle_lib.attention_qk(q, k, v, w.scale, causal)
+        dcheck(o, lse, o_ref, lse_ref, f"{w.name} splits={splits}")
+
+
+@pytest.mark.parametrize("nq", [1, 5])
+@pytest.mark.parametrize("d", [48, 112])
+def test_decode_guard_and_bounds(d, nq):
+    """NaN after K and V and around O: results bit-equal to plain
+    allocations, nothing outside O written."""
+    g = torch.Generator().manual_seed(21000 + d + nq)
+    q = torch.randn(1, 2, nq, d, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(1, 2, 1000, d, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(1, 2, 1000, d, generator=g).to(torch.bfloat16).cuda()
+    o1, l1 = fa.decode(q, k, v, causal=True)
+    pad = 1 << 14
+
+    def nan_backed(t):
+        buf = torch.full((t.numel() + pad,), float("nan"), dtype=t.dtype, device="cuda")
+        buf[: t.numel()].copy_(t.reshape(-1))
+        return buf[: t.numel()].view(t.shape)
+
+    kn, vn = nan_backed(k), nan_backed(v)
+    need = fa.fa_decode_workspace_size(1, 2, nq, 1000, d, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    obuf = torch.full((o1.numel() + 2 * pad,), float("nan"), dtype=o1.dtype, device="cuda")
+    o2 = obuf[pad: pad + o1.numel()].view(o1.shape)
+    l2 = torch.empty_like(l1)
+    rc = fa.fa_decode(q, kn, vn, o2, l2, 1, 2, nq, 1000, d, 1.0 / d ** 0.5, 1, 0, ws, need,
+                      torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert rc == fa.FA_OK
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and bool(torch.isfinite(o2.float()).all())
+    assert bool(torch.isnan(obuf[:pad].float()).all()) and bool(torch.isnan(obuf[pad + o1.numel():].float()).all())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", BWD_DIMS)
+def test_kv_outer(d, causal, oracle_lib):
+    from .test_gpu_kvouter import check as kcheck, run as krun
+
+    w = inputs.Workload(f"kvo_d{d}_{int(causal)}", 1, 2, 300, d, "bf16", "normal", causal,
+                        seed=22000 + d)
+    print(f"case {w.name}", flush=True)
+    q, k, v = inputs.make_qkv(w)
+    o, lse = krun(q, k, v, causal, w.scale)
+    o_ref, lse_ref = oracle_lib.attention(q, k, v, w.scale, causal)
+    kcheck(o, lse, o_ref, lse_ref, w.name)
