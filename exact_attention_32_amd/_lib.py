@@ -27,7 +27,7 @@ FA_ERR_STRIDE = 10
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_bwd", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_ex",
+EXPORTS = ("fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_ex",
            "fa_fwd_f32", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size", "fa_strerror")
 
 _lib = None
@@ -56,6 +56,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_ex.restype = i
+    lib.fa_bwd_ex.argtypes = [i] + [vp] * 10 + [i, i, i, i, f, i, ctypes.POINTER(ctypes.c_int64),
+                                                 vp]
     lib.fa_decode.restype = i
     lib.fa_decode.argtypes = [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t, vp]
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
@@ -115,6 +118,20 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal,
                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
                                      int(B), int(H), int(N), int(d), float(scale),
                                      int(bool(causal)), _stream(stream)))
+
+
+def fa_bwd_ex(dtype, q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, strides,
+              stream=None) -> int:
+    """Enqueue the backward pass on bf16 or fp16 strided views.  ``strides``
+    is a sequence of 24 element strides (q, k, v, o, dout, dq, dk, dv: batch,
+    head, row), or None for a NULL pointer.  Returns the fa_status code."""
+    arr = None
+    if strides is not None:
+        arr = (ctypes.c_int64 * 24)(*[int(x) for x in strides])
+    return int(load_library().fa_bwd_ex(int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                        _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                        int(B), int(H), int(N), int(d), float(scale),
+                                        int(bool(causal)), arr, _stream(stream)))
 
 
 def fa_fwd_ex(dtype, q, k, v, o, lse, B, H, N, d, scale, causal, strides, stream=None) -> int:
@@ -204,34 +221,47 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-             stream=None):
-    """Torch convenience wrapper of fa_bwd: q, k, v, o, dout are contiguous
-    bf16 [B, H, N, d] device tensors and (o, lse) what ``forward`` returned
-    for q, k, v with the same causal and scale.  Allocates dQ, dK, dV (bf16)
-    and the fp32 [B, H, N] workspace delta, enqueues the two kernels on
-    ``stream`` (default: the current torch stream) and returns
+             stream=None, out=None):
+    """Torch convenience wrapper of the backward pass: q, k, v, o, dout are
+    [B, H, N, d] device tensors, all bf16 or all fp16, and (o, lse) what
+    ``forward`` returned for q, k, v with the same causal and scale.  Dense
+    bf16 goes to fa_bwd; fp16 or strided views (last dimension contiguous) to
+    fa_bwd_ex.  Allocates dQ, dK, dV (dense, the input dtype) unless ``out``
+    gives them, and the fp32 [B, H, N] workspace delta; enqueues the two
+    kernels on ``stream`` (default: the current torch stream) and returns
     (dQ, dK, dV, delta)."""
     import torch
 
     ts = (q, k, v, o, dout)
     if not (all(t.shape == q.shape for t in ts) and q.dim() == 4):
         raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
-    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
-        raise TypeError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if not all(t.dtype == q.dtype for t in ts) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q, k, v, o, dout must all be bfloat16 or all float16")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
     if not all(t.is_cuda for t in ts + (lse,)):
         raise ValueError("all tensors must be device tensors")
-    if not all(t.is_contiguous() for t in ts + (lse,)):
-        raise ValueError("all tensors must be contiguous")
     B, H, N, d = q.shape
-    if lse.shape != (B, H, N):
-        raise ValueError("lse must be [B, H, N]")
+    if lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    dq, dk, dv = out
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+    tensors = ts + (dq, dk, dv)
+    if q.dtype == torch.bfloat16 and all(t.is_contiguous() for t in tensors):
+        rc = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+    else:
+        if any(t.stride(3) != 1 for t in tensors):
+            raise ValueError("the last dimension must be contiguous")
+        strides = [x for t in tensors for x in t.stride()[:3]]
+        dt = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+        rc = fa_bwd_ex(dt, q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal,
+                       strides, stream)
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return dq, dk, dv, delta

@@ -193,6 +193,56 @@ int fa_fwd_ex(int dtype, const void *q, const void *k, const void *v, void *o, f
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_bwd_ex(int dtype, const void *q, const void *k, const void *v, const void *o,
+              const void *dout, const float *lse, void *dq, void *dk, void *dv, float *delta,
+              int B, int H, int N, int d, float scale, int causal, const int64_t *strides,
+              hipStream_t stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta || !strides)
+        return FA_ERR_NULL;
+    if (!shape_ok(B, H, N, d)) {
+        if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return FA_ERR_SHAPE;
+        if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+        return FA_ERR_SHAPE;
+    }
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;
+    constexpr int kT = 8;  // q, k, v, o, dout, dq, dk, dv
+    for (int t = 0; t < kT; ++t) {
+        const int64_t *st = strides + 3 * t;
+        if (st[0] < 0 || st[1] < 0 || st[2] < d || st[2] > (1 << 24)) return FA_ERR_STRIDE;
+        if (st[0] > (int64_t)1 << 50 || st[1] > (int64_t)1 << 50) return FA_ERR_STRIDE;
+    }
+    for (const void *p : {q, k, v, o, dout, (const void *)lse, (const void *)dq, (const void *)dk,
+                          (const void *)dv, (const void *)delta})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    for (int t = 0; t < 3 * kT; ++t)
+        if (strides[t] % 8) return FA_ERR_ALIGN;
+    for (int t = 5; t < kT; ++t)
+        if (!rows_disjoint(strides + 3 * t, B, H, N, d)) return FA_ERR_STRIDE;
+    const uint64_t l_bytes = (uint64_t)B * H * N * 4u;
+    struct Span { const void *p; uint64_t n; };
+    const Span ins[6] = {{q, view_span(strides + 0, B, H, N, d)},
+                         {k, view_span(strides + 3, B, H, N, d)},
+                         {v, view_span(strides + 6, B, H, N, d)},
+                         {o, view_span(strides + 9, B, H, N, d)},
+                         {dout, view_span(strides + 12, B, H, N, d)},
+                         {lse, l_bytes}};
+    const Span outs[4] = {{dq, view_span(strides + 15, B, H, N, d)},
+                          {dk, view_span(strides + 18, B, H, N, d)},
+                          {dv, view_span(strides + 21, B, H, N, d)},
+                          {delta, l_bytes}};
+    for (const Span &w : outs)
+        for (const Span &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_ALIAS;
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return FA_ERR_ALIAS;
+    const hipError_t e = fa::launch_bwd_ex(dtype == FA_DTYPE_FP16, q, k, v, o, dout, lse, dq, dk,
+                                           dv, delta, B, H, N, d, scale, causal != 0, strides,
+                                           stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_fwd_kv_outer_workspace_size(int B, int H, int N, int d) {
     if (!shape_ok(B, H, N, d)) return 0;
     return (size_t)kvouter_workspace(B, H, N, d, nullptr, nullptr);

@@ -1,5 +1,6 @@
-// fa_bwd_bf16.hip -- backward pass of the fused attention for gfx950: bf16
-// Q, K, V, O, dO in; bf16 dQ, dK, dV out; fp32 scores, probabilities and
+// fa_bwd_bf16.hip -- backward pass of the fused attention for gfx950: Q, K,
+// V, O, dO in and dQ, dK, dV out, all bf16 (fa_bwd) or all bf16 or fp16 as
+// dense tensors or strided views (fa_bwd_ex); fp32 scores, probabilities and
 // accumulators.
 //
 // What is computed: the gradients of O = softmax(scale * Q K^T [+ causal
@@ -66,14 +67,41 @@ constexpr int kDkdvWaves = 2;
 template <int D>
 constexpr int kHalfUnroll = D == 128 ? 1 : 2;
 
-template <int DH, bool CAUSAL>
+// Element strides (batch, head, row) of the eight [B, H, N, d] tensors, d
+// contiguous, in the order of the enum below; LSE and delta stay dense
+// [B, H, N].  Used by the STRIDED instantiations only (the dense ones form
+// bh * N * d and d).
+enum BwdTensor { kTQ, kTK, kTV, kTO, kTDO, kTDQ, kTDK, kTDV, kTensors };
+struct BwdStrides {
+    long long b[kTensors], h[kTensors];
+    int n[kTensors];
+    int H;
+};
+
+// Element offset of head bh of tensor t, and its row stride.
+template <int DH, bool STRIDED>
+__device__ __forceinline__ size_t head_offset(const BwdStrides &st, int bh, int N, int t) {
+    if constexpr (STRIDED) {
+        const int b = bh / st.H, h = bh - b * st.H;
+        return (size_t)(b * st.b[t] + h * st.h[t]);
+    } else {
+        return (size_t)bh * (size_t)N * DH;
+    }
+}
+template <int DH, bool STRIDED>
+__device__ __forceinline__ int row_stride(const BwdStrides &st, int t) {
+    if constexpr (STRIDED) return st.n[t];
+    else return DH;
+}
+
+template <typename E, int DH, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kDqWaves<kLayout<DH>>, kDqWaves<kLayout<DH>>)))
-bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-              const __bf16 *__restrict__ V, const __bf16 *__restrict__ O,
-              const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
-              float *__restrict__ Delta, __bf16 *__restrict__ dQ, int N, int ntiles,
-              float scale, float scale_log2) {
+bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+              const E *__restrict__ O, const E *__restrict__ dO, const float *__restrict__ LSE,
+              float *__restrict__ Delta, E *__restrict__ dQ, int N, int ntiles, float scale,
+              float scale_log2, BwdStrides st) {
+    typedef typename TileOps<E>::x8 X8;
     constexpr int D = kLayout<DH>;
     constexpr int KS = DH / 16;  // k-steps of S^T and dP^T
     __shared__ __attribute__((aligned(16))) __bf16 lds_k0[kInner * D];
@@ -90,9 +118,9 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     int bh, qt;
     map_block(blockIdx.x, gridDim.x, ntiles, CAUSAL, bh, qt);
     const int r0 = qt * kOuter;
-    const size_t hoff = (size_t)bh * (size_t)N * DH;
-    const __bf16 *Kh = K + hoff;
-    const __bf16 *Vh = V + hoff;
+    const E *Kh = K + head_offset<DH, STRIDED>(st, bh, N, kTK);
+    const E *Vh = V + head_offset<DH, STRIDED>(st, bh, N, kTV);
+    const int kn = row_stride<DH, STRIDED>(st, kTK), vn = row_stride<DH, STRIDED>(st, kTV);
     const int wrow0 = r0 + wave * kRowsPerWave;
     const int qrow = wrow0 + j;
     const bool valid = qrow < N;
@@ -100,20 +128,26 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // Q^T and dO^T as B operands: lane (g, j) holds columns 16ks+8g..+7 of
     // its query row.  D_i = dO_i . O_i from the same columns, then summed
     // over the two half-waves.
-    bf16x8 qop[KS], doop[KS];
+    const E *Qr = Q + head_offset<DH, STRIDED>(st, bh, N, kTQ) +
+                  (size_t)qrow * row_stride<DH, STRIDED>(st, kTQ);
+    const E *dOr = dO + head_offset<DH, STRIDED>(st, bh, N, kTDO) +
+                   (size_t)qrow * row_stride<DH, STRIDED>(st, kTDO);
+    const E *Or = O + head_offset<DH, STRIDED>(st, bh, N, kTO) +
+                  (size_t)qrow * row_stride<DH, STRIDED>(st, kTO);
+    X8 qop[KS], doop[KS];
     float dpart = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
         if (valid) {
-            const size_t e = hoff + (size_t)qrow * DH + 16 * ks + 8 * g;
-            xq = load16(Q + e);
-            xd = load16(dO + e);
-            xo = load16(O + e);
+            const int e = 16 * ks + 8 * g;
+            xq = load16(Qr + e);
+            xd = load16(dOr + e);
+            xo = load16(Or + e);
         }
-        qop[ks] = __builtin_bit_cast(bf16x8, xq);
-        doop[ks] = __builtin_bit_cast(bf16x8, xd);
-        const bf16x8 ov = __builtin_bit_cast(bf16x8, xo);
+        qop[ks] = __builtin_bit_cast(X8, xq);
+        doop[ks] = __builtin_bit_cast(X8, xd);
+        const X8 ov = __builtin_bit_cast(X8, xo);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)doop[ks][e], (float)ov[e], dpart);
     }
@@ -129,7 +163,9 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const int kv_end = CAUSAL ? min(N, r0 + kOuter) : N;
     const int n_tiles = (kv_end + kInner - 1) / kInner;
 
-    const uint32_t src = tile_src_offset<D, DH>(wave, lane);
+    // K and V may have different row strides in a strided call.
+    const uint32_t ksrc = tile_src_offset<D, DH>(wave, lane, kn);
+    const uint32_t vsrc = STRIDED ? tile_src_offset<D, DH>(wave, lane, vn) : ksrc;
     const uint32_t rd = row_read_offset<D>(lane);
     uint32_t trd[2];
     tr_read_offsets<D>(lane, trd);
@@ -148,8 +184,8 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk, LDS3 char *nv) {
         const int c0 = t * kInner;
         if (t + 1 < n_tiles) {
-            load_tile<D, DH>(Kh, N, c0 + kInner, nk, src, wave);
-            load_tile<D, DH>(Vh, N, c0 + kInner, nv, src, wave);
+            load_tile<D, DH, STRIDED>(Kh, N, c0 + kInner, nk, ksrc, wave, kn);
+            load_tile<D, DH, STRIDED>(Vh, N, c0 + kInner, nv, vsrc, wave, vn);
         }
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
         if (active) {
@@ -164,10 +200,10 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 #pragma unroll
                 for (int kb = 0; kb < kInner / 32; ++kb) {
                     const uint32_t a = row_read_at(rd, ks) + kb * 32 * D * 2;
-                    const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(kt + a);
-                    const bf16x8 vf = *reinterpret_cast<const LDS3 bf16x8 *>(vt + a);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qop[ks], s[kb], 0, 0, 0);
-                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, doop[ks], dp[kb], 0, 0, 0);
+                    const X8 kf = *reinterpret_cast<const LDS3 X8 *>(kt + a);
+                    const X8 vf = *reinterpret_cast<const LDS3 X8 *>(vt + a);
+                    s[kb] = TileOps<E>::mfma(kf, qop[ks], s[kb]);
+                    dp[kb] = TileOps<E>::mfma(vf, doop[ks], dp[kb]);
                 }
             // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
             const bool need_mask = (CAUSAL && c0 + kInner - 1 > wrow0) || (c0 + kInner > N);
@@ -181,7 +217,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             }
             // dS^T = P^T o (dP^T - D), rounded to bf16 as the B operand of
             // the next product (rows 0-7 / 8-15 of a block are two k-steps).
-            bf16x8 dsop[kInner / 16];
+            X8 dsop[kInner / 16];
 #pragma unroll
             for (int kb = 0; kb < kInner / 32; ++kb) {
                 f32x8 lo, hi;
@@ -192,30 +228,32 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                     lo[r] = plo * (dp[kb][r] - delta);
                     hi[r] = phi * (dp[kb][r + 8] - delta);
                 }
-                dsop[2 * kb] = __builtin_convertvector(lo, bf16x8);
-                dsop[2 * kb + 1] = __builtin_convertvector(hi, bf16x8);
+                dsop[2 * kb] = __builtin_convertvector(lo, X8);
+                dsop[2 * kb + 1] = __builtin_convertvector(hi, X8);
             }
             // dQ^T += K^T dS^T; k-step T covers keys 16T .. 16T+15.
 #pragma unroll
             for (int T = 0; T < kInner / 16; ++T)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(kt, trd, T, db),
-                                                                      dsop[T], acc[db], 0, 0, 0);
+                    acc[db] = TileOps<E>::mfma(tr_read<D, X8>(kt, trd, T, db), dsop[T], acc[db]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
 
-    load_tile<D, DH>(Kh, N, 0, k0, src, wave);
-    load_tile<D, DH>(Vh, N, 0, v0, src, wave);
+    load_tile<D, DH, STRIDED>(Kh, N, 0, k0, ksrc, wave, kn);
+    load_tile<D, DH, STRIDED>(Vh, N, 0, v0, vsrc, wave, vn);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < n_tiles; t += 2) {
         step(t, k0, v0, k1, v1);
         if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
     }
-    if (valid) store_rows<D, DH>(dQ + hoff + (size_t)qrow * DH, acc, scale, g);
+    if (valid)
+        store_rows<D, DH>(dQ + head_offset<DH, STRIDED>(st, bh, N, kTDQ) +
+                              (size_t)qrow * row_stride<DH, STRIDED>(st, kTDQ),
+                          acc, scale, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -223,14 +261,14 @@ bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 // keys k0 + 32w .. +31 (lane (g, j) holds key j of the wave).  Query tiles
 // of 64 rows stream through LDS together with their LSE and D values.
 // ---------------------------------------------------------------------------
-template <int DH, bool CAUSAL>
+template <typename E, int DH, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kDkdvWaves<kLayout<DH>>, kDkdvWaves<kLayout<DH>>)))
-bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-                const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
-                const float *__restrict__ LSE, const float *__restrict__ Delta,
-                __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, int ntiles,
-                float scale, float scale_log2) {
+bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+                const E *__restrict__ dO, const float *__restrict__ LSE,
+                const float *__restrict__ Delta, E *__restrict__ dK, E *__restrict__ dV, int N,
+                int ntiles, float scale, float scale_log2, BwdStrides st) {
+    typedef typename TileOps<E>::x8 X8;
     constexpr int D = kLayout<DH>;
     constexpr int KS = DH / 16;  // k-steps of S and dP
     __shared__ __attribute__((aligned(16))) __bf16 lds_q0[kInner * D];
@@ -252,9 +290,9 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // are issued first (no reversal).
     map_block(blockIdx.x, gridDim.x, ntiles, false, bh, kt);
     const int k0 = kt * kOuter;
-    const size_t hoff = (size_t)bh * (size_t)N * DH;
-    const __bf16 *Qh = Q + hoff;
-    const __bf16 *dOh = dO + hoff;
+    const E *Qh = Q + head_offset<DH, STRIDED>(st, bh, N, kTQ);
+    const E *dOh = dO + head_offset<DH, STRIDED>(st, bh, N, kTDO);
+    const int qn = row_stride<DH, STRIDED>(st, kTQ), don = row_stride<DH, STRIDED>(st, kTDO);
     const float *LSEh = LSE + (size_t)bh * N;
     const float *Dh = Delta + (size_t)bh * N;
     const int wk0 = k0 + wave * kRowsPerWave;
@@ -262,24 +300,30 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const bool valid = key < N;
 
     // K^T and V^T as B operands: lane (g, j) holds columns 16ks+8g..+7 of its key.
-    bf16x8 kop[KS], vop[KS];
+    const E *Kr = K + head_offset<DH, STRIDED>(st, bh, N, kTK) +
+                  (size_t)key * row_stride<DH, STRIDED>(st, kTK);
+    const E *Vr = V + head_offset<DH, STRIDED>(st, bh, N, kTV) +
+                  (size_t)key * row_stride<DH, STRIDED>(st, kTV);
+    X8 kop[KS], vop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
         if (valid) {
-            const size_t e = hoff + (size_t)key * DH + 16 * ks + 8 * g;
-            xk = load16(K + e);
-            xv = load16(V + e);
+            const int e = 16 * ks + 8 * g;
+            xk = load16(Kr + e);
+            xv = load16(Vr + e);
         }
-        kop[ks] = __builtin_bit_cast(bf16x8, xk);
-        vop[ks] = __builtin_bit_cast(bf16x8, xv);
+        kop[ks] = __builtin_bit_cast(X8, xk);
+        vop[ks] = __builtin_bit_cast(X8, xv);
     }
 
     // Causal: the query tiles before the workgroup's first key see none of its keys.
     const int t_begin = CAUSAL ? k0 / kInner : 0;
     const int n_tiles = (N + kInner - 1) / kInner;
 
-    const uint32_t src = tile_src_offset<D, DH>(wave, lane);
+    // Q and dO may have different row strides in a strided call.
+    const uint32_t qsrc = tile_src_offset<D, DH>(wave, lane, qn);
+    const uint32_t dosrc = STRIDED ? tile_src_offset<D, DH>(wave, lane, don) : qsrc;
     const uint32_t rd = row_read_offset<D>(lane);
     uint32_t trd[2];
     tr_read_offsets<D>(lane, trd);
@@ -298,8 +342,8 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // Rows c0 .. c0+63 of Q and dO, and their LSE and D (waves 0 and 1 copy
     // those, one 4-byte direct-to-LDS load each; entries past N read as 0).
     auto load_all = [&](int c0, LDS3 char *dq_, LDS3 char *do_, LDS3 float *st) {
-        load_tile<D, DH>(Qh, N, c0, dq_, src, wave);
-        load_tile<D, DH>(dOh, N, c0, do_, src, wave);
+        load_tile<D, DH, STRIDED>(Qh, N, c0, dq_, qsrc, wave, qn);
+        load_tile<D, DH, STRIDED>(dOh, N, c0, do_, dosrc, wave, don);
         if (wave < 2) load_vec(wave == 0 ? LSEh : Dh, N, c0, st + wave * kInner, lane);
     };
 
@@ -318,10 +362,10 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const uint32_t a = row_read_at(rd, ks) + qb * 32 * D * 2;
-                    const bf16x8 qf = *reinterpret_cast<const LDS3 bf16x8 *>(qt_ + a);
-                    const bf16x8 of = *reinterpret_cast<const LDS3 bf16x8 *>(ot_ + a);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kop[ks], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vop[ks], dp, 0, 0, 0);
+                    const X8 qf = *reinterpret_cast<const LDS3 X8 *>(qt_ + a);
+                    const X8 of = *reinterpret_cast<const LDS3 X8 *>(ot_ + a);
+                    s = TileOps<E>::mfma(qf, kop[ks], s);
+                    dp = TileOps<E>::mfma(of, vop[ks], dp);
                 }
                 const int qbase = c0 + 32 * qb;
                 const bool need_mask = (CAUSAL && qbase < wk0 + kRowsPerWave - 1) || (qbase + 32 > N);
@@ -347,18 +391,18 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                         else { phi[r - 8] = p; dhi[r - 8] = ds; }
                     }
                 }
-                const bf16x8 pop[2] = {__builtin_convertvector(plo, bf16x8), __builtin_convertvector(phi, bf16x8)};
-                const bf16x8 dsop[2] = {__builtin_convertvector(dlo, bf16x8), __builtin_convertvector(dhi, bf16x8)};
+                const X8 pop[2] = {__builtin_convertvector(plo, X8), __builtin_convertvector(phi, X8)};
+                const X8 dsop[2] = {__builtin_convertvector(dlo, X8), __builtin_convertvector(dhi, X8)};
                 // dV^T += dO^T P and dK^T += Q^T dS over the half's 32 queries
                 // (k-steps T = 2qb, 2qb + 1).
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
-                        accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(ot_, trd, 2 * qb + h, db),
-                                                                           pop[h], accv[db], 0, 0, 0);
-                        acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(qt_, trd, 2 * qb + h, db),
-                                                                           dsop[h], acck[db], 0, 0, 0);
+                        accv[db] = TileOps<E>::mfma(tr_read<D, X8>(ot_, trd, 2 * qb + h, db), pop[h],
+                                                    accv[db]);
+                        acck[db] = TileOps<E>::mfma(tr_read<D, X8>(qt_, trd, 2 * qb + h, db), dsop[h],
+                                                    acck[db]);
                     }
             }
         }
@@ -378,44 +422,47 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         }
     }
     if (valid) {
-        store_rows<D, DH>(dK + hoff + (size_t)key * DH, acck, scale, g);
-        store_rows<D, DH>(dV + hoff + (size_t)key * DH, accv, 1.f, g);
+        store_rows<D, DH>(dK + head_offset<DH, STRIDED>(st, bh, N, kTDK) +
+                              (size_t)key * row_stride<DH, STRIDED>(st, kTDK),
+                          acck, scale, g);
+        store_rows<D, DH>(dV + head_offset<DH, STRIDED>(st, bh, N, kTDV) +
+                              (size_t)key * row_stride<DH, STRIDED>(st, kTDV),
+                          accv, 1.f, g);
     }
 }
 
-template <int D, bool CAUSAL>
+template <typename E, int DH, bool CAUSAL, bool STRIDED>
 hipError_t launch(const void *q, const void *k, const void *v, const void *o, const void *dout,
                   const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
-                  int N, float scale, hipStream_t stream) {
+                  int N, float scale, const BwdStrides &st, hipStream_t stream) {
     const int ntiles = (N + kOuter - 1) / kOuter;
     const int blocks = B * H * ntiles;
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    const __bf16 *Q = static_cast<const __bf16 *>(q), *K = static_cast<const __bf16 *>(k),
-                 *V = static_cast<const __bf16 *>(v), *O = static_cast<const __bf16 *>(o),
-                 *dO = static_cast<const __bf16 *>(dout);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream, Q, K,
-                       V, O, dO, lse, delta, static_cast<__bf16 *>(dq), N, ntiles, scale,
-                       scale_log2);
+    const E *Q = static_cast<const E *>(q), *K = static_cast<const E *>(k),
+            *V = static_cast<const E *>(v), *O = static_cast<const E *>(o),
+            *dO = static_cast<const E *>(dout);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, DH, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads), 0,
+                       stream, Q, K, V, O, dO, lse, delta, static_cast<E *>(dq), N, ntiles, scale,
+                       scale_log2, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(blocks), dim3(kThreads), 0, stream, Q,
-                       K, V, dO, lse, delta, static_cast<__bf16 *>(dk), static_cast<__bf16 *>(dv),
-                       N, ntiles, scale, scale_log2);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, DH, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads), 0,
+                       stream, Q, K, V, dO, lse, delta, static_cast<E *>(dk),
+                       static_cast<E *>(dv), N, ntiles, scale, scale_log2, st);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
-                           const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                           float *delta, int B, int H, int N, int d, float scale, bool causal,
-                           hipStream_t stream) {
+template <typename E, bool STRIDED>
+hipError_t launch_d(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                    const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int H,
+                    int N, int d, float scale, bool causal, const BwdStrides &st,
+                    hipStream_t stream) {
 #define FA_BWD_CASE(DH)                                                                          \
     case DH:                                                                                     \
-        return causal ? launch<DH, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale,  \
-                                         stream)                                                 \
-                      : launch<DH, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, scale, \
-                                          stream)
+        return causal ? launch<E, DH, true, STRIDED>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, \
+                                                     H, N, scale, st, stream)                    \
+                      : launch<E, DH, false, STRIDED>(q, k, v, o, dout, lse, dq, dk, dv, delta,  \
+                                                      B, H, N, scale, st, stream)
     switch (d) {
         FA_BWD_CASE(16);
         FA_BWD_CASE(32);
@@ -424,13 +471,47 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
         FA_BWD_CASE(80);
         FA_BWD_CASE(96);
         FA_BWD_CASE(112);
-        default:
-            return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
-                                              scale, stream)
-                          : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
-                                               scale, stream);
+        FA_BWD_CASE(128);
+        default: return hipErrorInvalidValue;
     }
 #undef FA_BWD_CASE
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
+                           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                           float *delta, int B, int H, int N, int d, float scale, bool causal,
+                           hipStream_t stream) {
+    const BwdStrides none = {};
+    return launch_d<__bf16, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale,
+                                   causal, none, stream);
+}
+
+hipError_t launch_bwd_ex(bool fp16, const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                         float *delta, int B, int H, int N, int d, float scale, bool causal,
+                         const int64_t *strides, hipStream_t stream) {
+    const long long hd = (long long)N * d, bd = (long long)H * hd;
+    bool dense = true;
+    BwdStrides st;
+    for (int t = 0; t < kTensors; ++t) {
+        const int64_t *x = strides + 3 * t;
+        dense = dense && x[0] == bd && x[1] == hd && x[2] == d;
+        st.b[t] = x[0];
+        st.h[t] = x[1];
+        st.n[t] = (int)x[2];
+    }
+    st.H = H;
+    if (fp16)
+        return dense ? launch_d<_Float16, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
+                                                 d, scale, causal, st, stream)
+                     : launch_d<_Float16, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N,
+                                                d, scale, causal, st, stream);
+    return dense ? launch_d<__bf16, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d,
+                                           scale, causal, st, stream)
+                 : launch_d<__bf16, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d,
+                                          scale, causal, st, stream);
 }
 
 }  // namespace fa

@@ -30,6 +30,14 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            float *delta, int B, int H, int N, int d, float scale, bool causal,
                            hipStream_t stream);
 
+// The backward pass on bf16 (fp16 = false) or fp16 views with element
+// strides (q, k, v, o, dout, dq, dk, dv: batch, head, row; d contiguous);
+// lse and delta dense.  The dense layout takes the contiguous kernels.
+hipError_t launch_bwd_ex(bool fp16, const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                         float *delta, int B, int H, int N, int d, float scale, bool causal,
+                         const int64_t *strides, hipStream_t stream);
+
 // Forward pass in the key/value-outer order of Algorithm 1: one launch per
 // 64-key block; ows [B,H,N,d], lws, mws [B,H,N] (fp32) carry O, l, m between
 // launches.

@@ -1,8 +1,9 @@
 // fa_tiles.h -- device helpers shared by the kernels that stream 64-row
-// tiles of a [N, d] bf16 matrix through LDS with 256-thread workgroups and
-// read them both row-wise (MFMA A operands of 32 x 16 blocks) and transposed
-// (ds_read_b64_tr_b16): the swizzle, the direct-to-LDS tile copy, the lane
-// read offsets, and the store of a [d x 32] accumulator block as bf16 rows.
+// tiles of a [N, d] bf16 or fp16 matrix through LDS with 256-thread
+// workgroups and read them both row-wise (MFMA A operands of 32 x 16 blocks)
+// and transposed (ds_read_b64_tr_b16): the swizzle, the direct-to-LDS tile
+// copy, the lane read offsets, the element types' MFMA, and the store of a
+// [d x 32] accumulator block as rows of the element type.
 // Not part of the public interface.
 #pragma once
 
@@ -14,6 +15,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -28,6 +31,27 @@ constexpr int kRowsPerWave = 32;            // rows (queries or keys) owned by o
 constexpr int kOuter = kWaves * kRowsPerWave;  // rows owned by one workgroup
 constexpr int kInner = 64;                  // rows per streamed tile
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Operand vectors and the 32x32x16 MFMA (fp32 accumulation) of an element
+// type.
+template <typename E>
+struct TileOps;
+template <>
+struct TileOps<__bf16> {
+    typedef bf16x8 x8;
+    typedef bf16x4 x4;
+    static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct TileOps<_Float16> {
+    typedef f16x8 x8;
+    typedef f16x4 x4;
+    static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 // One swizzle for tiles read both by 128-bit row reads (16 rows x one 16-byte
 // chunk per LDS pass) and by the 64-bit transpose read (4 rows x 4 chunks per
@@ -57,28 +81,35 @@ __device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse
     if (reverse) tile = ntiles - 1 - tile;
 }
 
-// Direct-to-LDS copy of one kInner-row tile of a [N, DH] bf16 matrix (rows
-// r0 .. r0 + kInner - 1; rows >= N read as zeros) into `dst`, a tile of
-// kInner rows of D >= DH columns, swizzled: lane l of load u of wave w
-// writes chunk position q = (u*kWaves + w)*64 + l, and fetches the logical
-// chunk that the swizzle stores there.  Load u covers the rows 16 (D = 128)
-// or 32 (D = 64) after load 0's, which leaves the row's swizzle term
-// unchanged, so one lane offset `src` (load 0) serves every load, moved by
-// that many rows of DH elements.  With DH < D the columns at and past DH
-// receive the next row's leading elements (or zeros past the tile's last
-// row): callers use them only for output rows they never store.
-template <int D, int DH = D>
-__device__ __forceinline__ void load_tile(const __bf16 *mat, int N, int r0, LDS3 char *dst,
-                                          uint32_t src, int wave) {
+// Direct-to-LDS copy of one kInner-row tile of a [N, DH] matrix of 2-byte
+// elements, rows `rs` elements apart (rows r0 .. r0 + kInner - 1; rows >= N
+// read as zeros) into `dst`, a tile of kInner rows of D >= DH columns,
+// swizzled: lane l of load u of wave w writes chunk position
+// q = (u*kWaves + w)*64 + l, and fetches the logical chunk that the swizzle
+// stores there.  Load u covers the rows 16 (D = 128) or 32 (D = 64) after
+// load 0's, which leaves the row's swizzle term unchanged, so one lane
+// offset `src` (load 0, tile_src_offset) serves every load, moved by that
+// many rows.  The descriptor ends after the last valid row's DH elements.
+// With DH < D the columns at and past DH receive copies of the same row's
+// leading chunks (see tile_src_offset): callers use them only for output
+// rows they never store.
+template <int D, int DH = D, bool STRIDED = false>
+__device__ __forceinline__ void load_tile(const void *mat, int N, int r0, LDS3 char *dst,
+                                          uint32_t src, int wave, int rs = DH) {
     static_assert(DH <= D && DH % 16 == 0, "row length");
     constexpr int kLoads = kInner * (D / 8) / kThreads;
     constexpr int kRowsPerLoad = kWaves * 1024 / (D * 2);
-    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - r0)) * (uint32_t)(DH * 2);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat + (size_t)r0 * DH, bytes);
+    const int stride = STRIDED ? rs : DH;
+    const uint32_t rows = (uint32_t)max(0, min(kInner, N - r0));
+    const uint32_t bytes = STRIDED ? (rows ? (rows - 1) * (uint32_t)rs * 2u + DH * 2u : 0u)
+                                   : rows * (uint32_t)(DH * 2);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        make_rsrc((const char *)mat + (size_t)r0 * (size_t)stride * 2, bytes);
 #pragma unroll
     for (int u = 0; u < kLoads; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)(dst + (u * kWaves + wave) * 1024),
-                                                 16, src, u * kRowsPerLoad * DH * 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc,
+                                                 (LDS3 void *)(dst + (u * kWaves + wave) * 1024), 16,
+                                                 src, u * kRowsPerLoad * stride * 2, 0, 0);
 }
 
 // Direct-to-LDS copy of vec[c0 .. c0 + 63] (fp32; entries at or past N read
@@ -90,13 +121,18 @@ __device__ __forceinline__ void load_vec(const float *vec, int N, int c0, LDS3 f
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
 }
 
-// Lane source offset of load_tile's first load (see there).
+// Lane source offset of load_tile's first load (see there), rows `rs`
+// elements apart.  A position whose logical chunk c lies at or past DH/8
+// fetches chunk c mod DH/8 of the same row: every byte read belongs to a
+// row of the matrix.
 template <int D, int DH = D>
-__device__ __forceinline__ uint32_t tile_src_offset(int wave, int lane) {
+__device__ __forceinline__ uint32_t tile_src_offset(int wave, int lane, int rs = DH) {
     const int q = wave * 64 + lane;
     const int r = q / (D / 8);
     const int p = q % (D / 8);
-    return (uint32_t)(r * DH * 2 + ((p ^ swz<D>(r)) << 4));
+    int c = p ^ swz<D>(r);
+    if (DH < D) c %= DH / 8;
+    return (uint32_t)(r * rs * 2 + (c << 4));
 }
 
 // Byte offset (within a tile) of the 128-bit operand read of k-step ks: lane
@@ -131,25 +167,24 @@ __device__ __forceinline__ void tr_read_offsets(int lane, uint32_t *off) {
     }
 }
 
-template <int D>
-__device__ __forceinline__ bf16x8 tr_read(const LDS3 char *tile, const uint32_t *off, int T,
-                                          int db) {
+template <int D, typename X8 = bf16x8>
+__device__ __forceinline__ X8 tr_read(const LDS3 char *tile, const uint32_t *off, int T, int db) {
     const LDS3 char *base = tile + T * 16 * D * 2;
     const uint32_t x = (uint32_t)(db << 6);
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + (off[0] ^ x)));
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + (off[1] ^ x)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__device__ __forceinline__ u32x4 load16(const __bf16 *p) {
+__device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
 // Store a [D x 32] accumulator block set (lane (g, j) holds row `row` of the
-// result, columns 32db + 8a + 4g + e in acc[db][4a + e]) times `mul` as bf16;
-// only the first DH columns are stored.
-template <int D, int DH = D>
-__device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, float mul, int g) {
+// result, columns 32db + 8a + 4g + e in acc[db][4a + e]) times `mul` as the
+// element type E; only the first DH columns are stored.
+template <int D, int DH = D, typename E = __bf16>
+__device__ __forceinline__ void store_rows(E *row_ptr, const f32x16 *acc, float mul, int g) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -158,8 +193,9 @@ __device__ __forceinline__ void store_rows(__bf16 *row_ptr, const f32x16 *acc, f
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * mul;
-            *reinterpret_cast<bf16x4 *>(row_ptr + 32 * db + 8 * a + 4 * g) =
-                __builtin_convertvector(x, bf16x4);
+            typedef typename TileOps<E>::x4 X4;
+            *reinterpret_cast<X4 *>(row_ptr + 32 * db + 8 * a + 4 * g) =
+                __builtin_convertvector(x, X4);
         }
 }
 

@@ -193,6 +193,33 @@ int fa_fwd_ex(int dtype, const void *q, const void *k, const void *v, void *o, f
               const int64_t *strides, hipStream_t stream);
 
 /*
+ * fa_bwd_ex -- fa_bwd generalised the way fa_fwd_ex generalises fa_fwd:
+ * fp16 as well as bf16 tensors, and strided views (the Triton page's kernel
+ * interface, "手写 FlashAttention", section 3.4; its section 5.1 on the
+ * backward pass).
+ *
+ *   dtype   : FA_DTYPE_BF16 or FA_DTYPE_FP16 -- the type of q, k, v, o,
+ *             dout, dq, dk and dv (products on that type's MFMA, P and dS
+ *             rounded to it before the products that take them; scores,
+ *             statistics and accumulation fp32; gradients rounded to
+ *             nearest even)
+ *   strides : host array of 24 element strides, for q, k, v, o, dout, dq,
+ *             dk, dv in turn: batch, head, row (the d elements of a row
+ *             contiguous), with the rules of fa_fwd_ex; the rows of dq, dk
+ *             and dv must not overlap each other.  lse and delta stay dense
+ *             fp32 [B, H, N].
+ * Other arguments, ownership and errors as for fa_bwd, plus FA_ERR_DTYPE and
+ * FA_ERR_STRIDE; no part of dq, dk, dv or delta may overlap an input or
+ * another output.  fp16 holds dS = P (dP - delta) and the gradients, so
+ * |dO| |V| and the gradients must stay within fp16's range.  With the dense
+ * strides and dtype bf16 this runs exactly fa_bwd's kernels.
+ */
+int fa_bwd_ex(int dtype, const void *q, const void *k, const void *v, const void *o,
+              const void *dout, const float *lse, void *dq, void *dk, void *dv, float *delta,
+              int B, int H, int N, int d, float scale, int causal, const int64_t *strides,
+              hipStream_t stream);
+
+/*
  * fa_fwd_kv_outer -- the same result as fa_fwd (O and LSE, bf16 in/out) in
  * the loop order of Algorithm 1 of "解析 FlashAttention（2）：FlashAttention-v1
  * 前向传播" (section 4): key/value blocks outside, query blocks inside, the

@@ -224,3 +224,36 @@ def test_fwd_ex_validation_codes(lib):
     assert call(strides=bshd, o=K + 64) == fa.FA_ERR_ALIAS
     assert call(strides=bshd, lse=V + 1024) == fa.FA_ERR_ALIAS
     assert call(strides=bshd, q=Q + 8) == fa.FA_ERR_ALIGN
+
+
+def test_bwd_ex_validation_codes(lib):
+    B, H, N, d = 2, 3, 100, 64
+    dense = [H * N * d, N * d, d] * 8
+    bshd = [N * H * d, d, H * d] * 8           # [B, N, H, d] memory order
+
+    def call(dtype=fa.FA_DTYPE_BF16, strides=dense, **kw):
+        p = dict(q=BQ, k=BK, v=BV, o=BO, dout=BD, lse=BL, dq=BDQ, dk=BDK, dv=BDV, delta=BDL)
+        p.update(kw)
+        return fa.fa_bwd_ex(dtype, p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"],
+                            p["dk"], p["dv"], p["delta"], B, H, N, d, 0.125, 1, strides, None)
+    assert call(strides=None) == fa.FA_ERR_NULL
+    for name in ("q", "dout", "lse", "dv", "delta"):
+        assert call(**{name: 0}) == fa.FA_ERR_NULL, name
+    assert call(dtype=2) == fa.FA_ERR_DTYPE
+    bad = list(dense); bad[2] = 32                 # q row stride < d
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[14] = 1 << 25           # dout row stride > 2^24
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[18] = -8                # dk batch stride < 0
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[4] = N * d + 4          # k head stride not a multiple of 8
+    assert call(strides=bad) == fa.FA_ERR_ALIGN
+    assert call(dq=BDQ + 8) == fa.FA_ERR_ALIGN
+    bad = list(dense); bad[21:24] = [H * N * d, 8 * d, d]   # dv heads overlap
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    shared = list(dense); shared[3:5] = [N * d, 0]           # k shared by all heads: allowed
+    assert call(strides=shared, dq=BQ) == fa.FA_ERR_ALIAS    # (fails on the alias only)
+    assert call(strides=bshd, dk=BV + 64) == fa.FA_ERR_ALIAS
+    assert call(strides=bshd, delta=BL + 64) == fa.FA_ERR_ALIAS
+    assert call(strides=bshd, dv=BDQ + 128) == fa.FA_ERR_ALIAS   # outputs overlap
+    assert call(strides=bshd, q=BQ + 8) == fa.FA_ERR_ALIGN
