@@ -27,8 +27,9 @@ FA_ERR_STRIDE = 10
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_ex",
-           "fa_fwd_f32", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size", "fa_strerror")
+EXPORTS = ("fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_ex", "fa_decode_workspace_size",
+           "fa_fwd", "fa_fwd_ex", "fa_fwd_f32", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size",
+           "fa_strerror")
 
 _lib = None
 
@@ -61,6 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                  vp]
     lib.fa_decode.restype = i
     lib.fa_decode.argtypes = [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t, vp]
+    lib.fa_decode_ex.restype = i
+    lib.fa_decode_ex.argtypes = ([i] + [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t,
+                                                             ctypes.POINTER(ctypes.c_int64), vp])
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_decode_workspace_size.argtypes = [i] * 6
     lib.fa_fwd_ex.restype = i
@@ -170,6 +174,21 @@ def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, works
                                         int(workspace_bytes), _stream(stream)))
 
 
+def fa_decode_ex(dtype, q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace,
+                 workspace_bytes, strides, stream=None) -> int:
+    """Enqueue the decode pass on bf16 or fp16 strided views.  ``strides`` is
+    a sequence of 12 element strides (q, k, v, o: batch, head, row), or None
+    for a NULL pointer.  Returns the fa_status code."""
+    arr = None
+    if strides is not None:
+        arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    return int(load_library().fa_decode_ex(int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                           _ptr(lse), int(B), int(H), int(Nq), int(Nk), int(d),
+                                           float(scale), int(bool(causal)), int(num_splits),
+                                           _ptr(workspace), int(workspace_bytes), arr,
+                                           _stream(stream)))
+
+
 def fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits=0) -> int:
     return int(load_library().fa_decode_workspace_size(int(B), int(H), int(Nq), int(Nk),
                                                        int(d), int(num_splits)))
@@ -268,20 +287,23 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
 
 
 def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
-           stream=None):
-    """Torch convenience wrapper of fa_decode: q is a contiguous bf16
-    [B, H, Nq, d] device tensor (Nq <= 16), k and v contiguous bf16
-    [B, H, Nk, d].  Allocates O, LSE and the workspace, enqueues the kernels
-    on ``stream`` (default: the current torch stream) and returns (O, LSE)."""
+           stream=None, out=None):
+    """Torch convenience wrapper of the decode pass: q is a [B, H, Nq, d]
+    device tensor (Nq <= 16), k and v [B, H, Nk, d], all bf16 or all fp16.
+    Dense bf16 goes to fa_decode; fp16 or strided views (last dimension
+    contiguous; e.g. a [B, Nk, H, d] key/value cache) to fa_decode_ex.
+    Allocates O (dense, the input dtype) unless ``out`` gives it, LSE and the
+    workspace, enqueues the kernels on ``stream`` (default: the current torch
+    stream) and returns (O, LSE)."""
     import torch
 
     if not (q.dim() == k.dim() == 4 and k.shape == v.shape and q.shape[:2] == k.shape[:2]
             and q.shape[3] == k.shape[3]):
         raise ValueError("need q [B, H, Nq, d] and k, v [B, H, Nk, d]")
-    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
-        raise TypeError("q, k, v must be bfloat16")
-    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
-        raise ValueError("q, k, v must be contiguous device tensors")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q, k, v must all be bfloat16 or all float16")
+    if not all(t.is_cuda for t in (q, k, v)):
+        raise ValueError("q, k, v must be device tensors")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if scale is None:
@@ -290,11 +312,21 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits
     if need == 0:
         raise FAError(FA_ERR_SHAPE, fa_strerror(FA_ERR_SHAPE))
     ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device) if out is None else out
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    rc = fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, ws, need, stream)
+    tensors = (q, k, v, o)
+    if q.dtype == torch.bfloat16 and all(t.is_contiguous() for t in tensors):
+        rc = fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, ws, need,
+                       stream)
+    else:
+        if any(t.stride(3) != 1 for t in tensors):
+            raise ValueError("the last dimension must be contiguous")
+        strides = [x for t in tensors for x in t.stride()[:3]]
+        dt = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+        rc = fa_decode_ex(dt, q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, ws,
+                          need, strides, stream)
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return o, lse

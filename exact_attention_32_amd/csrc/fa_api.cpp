@@ -309,6 +309,52 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_decode_ex(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                 void *workspace, size_t workspace_bytes, const int64_t *strides,
+                 hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !strides) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 1 || Nq > fa::kDecodeMaxQueries || Nk < Nq || Nk > (1 << 30))
+        return FA_ERR_SHAPE;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;
+    for (int t = 0; t < 4; ++t) {
+        const int64_t *st = strides + 3 * t;
+        if (st[0] < 0 || st[1] < 0 || st[2] < d || st[2] > (1 << 24)) return FA_ERR_STRIDE;
+        if (st[0] > (int64_t)1 << 50 || st[1] > (int64_t)1 << 50) return FA_ERR_STRIDE;
+    }
+    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    uint64_t lse_off = 0;
+    const uint64_t need = decode_workspace(B, H, Nq, d, S, &lse_off);
+    if (!workspace || (uint64_t)workspace_bytes < need) return FA_ERR_WORKSPACE;
+    for (const void *p : {q, k, v, (const void *)o, (const void *)lse, (const void *)workspace})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    for (int t = 0; t < 12; ++t)
+        if (strides[t] % 8) return FA_ERR_ALIGN;
+    if (!rows_disjoint(strides + 9, B, H, Nq, d)) return FA_ERR_STRIDE;
+    const uint64_t l_bytes = (uint64_t)B * H * Nq * 4;
+    struct Span { const void *p; uint64_t n; };
+    const Span ins[] = {{q, view_span(strides + 0, B, H, Nq, d)},
+                        {k, view_span(strides + 3, B, H, Nk, d)},
+                        {v, view_span(strides + 6, B, H, Nk, d)}};
+    const Span outs[] = {{o, view_span(strides + 9, B, H, Nq, d)}, {lse, l_bytes},
+                         {workspace, need}};
+    for (const Span &w : outs)
+        for (const Span &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_ALIAS;
+    for (int a = 0; a < 3; ++a)
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return FA_ERR_ALIAS;
+    float *o_part = static_cast<float *>(workspace);
+    float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
+    const hipError_t e = fa::launch_decode_ex(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B, H, Nq,
+                                              Nk, d, scale, causal != 0, S, o_part, lse_part,
+                                              strides, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char *fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";

@@ -1,5 +1,6 @@
 // fa_decode_bf16.hip -- attention of a few queries over many keys (decode)
-// for gfx950: bf16 Q, K, V, O; fp32 scores, softmax statistics and sums.
+// for gfx950: bf16 Q, K, V, O (fa_decode), or bf16 or fp16 dense tensors or
+// strided views (fa_decode_ex); fp32 scores, softmax statistics and sums.
 //
 // What is computed: O = softmax(scale * Q K^T [+ mask]) V and the per-row
 // log-sum-exp for Nq <= 16 queries over Nk keys of each (batch, head), the
@@ -40,8 +41,48 @@
 namespace fa {
 namespace {
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// The two 2-byte elements of a 32-bit word (low half first), widened to fp32.
+template <typename E>
+__device__ __forceinline__ float elem_lo(uint32_t w);
+template <typename E>
+__device__ __forceinline__ float elem_hi(uint32_t w);
+template <>
+__device__ __forceinline__ float elem_lo<__bf16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <>
+__device__ __forceinline__ float elem_hi<__bf16>(uint32_t w) {
+    return __uint_as_float(w & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ float elem_lo<_Float16>(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <>
+__device__ __forceinline__ float elem_hi<_Float16>(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Element strides (batch, head, row) of q, k, v, o (d contiguous) for the
+// STRIDED instantiations; the dense ones form bh * rows * d and d.
+enum DecTensor { kDQ, kDK, kDV, kDO, kDecTensors };
+struct DecStrides {
+    long long b[kDecTensors], h[kDecTensors];
+    int n[kDecTensors];
+    int H;
+};
+template <int DH, bool STRIDED>
+__device__ __forceinline__ size_t dec_head_offset(const DecStrides &st, int bh, int rows, int t) {
+    if constexpr (STRIDED) {
+        const int b = bh / st.H, h = bh - b * st.H;
+        return (size_t)(b * st.b[t] + h * st.h[t]);
+    } else {
+        return (size_t)bh * (size_t)rows * DH;
+    }
+}
+template <int DH, bool STRIDED>
+__device__ __forceinline__ int dec_row_stride(const DecStrides &st, int t) {
+    if constexpr (STRIDED) return st.n[t];
+    else return DH;
+}
 
 __device__ __forceinline__ float dpp_add(float x, int ctrl_sel) {
     // ctrl values: quad_perm [1,0,3,2] = 0xb1, quad_perm [2,3,0,1] = 0x4e,
@@ -98,12 +139,11 @@ constexpr int kDecodeWaves = (NQ + 3) / 4;
 template <int DH>
 constexpr int kDecLayout = DH <= 64 ? 64 : 128;
 
-template <int DH, int NQ, bool CAUSAL>
+template <typename E, int DH, int NQ, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(64 * kDecodeWaves<NQ>)
-decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-                    const __bf16 *__restrict__ V, float *__restrict__ o_part,
-                    float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
-                    float scale_log2) {
+decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+                    float *__restrict__ o_part, float *__restrict__ lse_part, int Nq, int Nk,
+                    int S, int chunk, float scale, float scale_log2, DecStrides st) {
     constexpr int D = kDecLayout<DH>;
     constexpr int G = D / 8;       // lanes per key row
     constexpr int RPW = 64 / G;    // rows per load instruction
@@ -127,11 +167,13 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     for (int qi = 0; qi < NQW; ++qi) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (qbase + qi < Nq && has_cols)
-            w = *reinterpret_cast<const u32x4 *>(Q + ((size_t)bh * Nq + qbase + qi) * DH + col * 8);
+            w = *reinterpret_cast<const u32x4 *>(
+                Q + dec_head_offset<DH, STRIDED>(st, bh, Nq, kDQ) +
+                (size_t)(qbase + qi) * dec_row_stride<DH, STRIDED>(st, kDQ) + col * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            qf[qi][2 * e] = bf16_lo(w[e]);
-            qf[qi][2 * e + 1] = bf16_hi(w[e]);
+            qf[qi][2 * e] = elem_lo<E>(w[e]);
+            qf[qi][2 * e + 1] = elem_hi<E>(w[e]);
         }
     }
     float m[NQW], l[NQW], acc[NQW][8];
@@ -143,8 +185,9 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
     }
 
-    const __bf16 *Kh = K + (size_t)bh * Nk * DH + col * 8;
-    const __bf16 *Vh = V + (size_t)bh * Nk * DH + col * 8;
+    const E *Kh = K + dec_head_offset<DH, STRIDED>(st, bh, Nk, kDK) + col * 8;
+    const E *Vh = V + dec_head_offset<DH, STRIDED>(st, bh, Nk, kDV) + col * 8;
+    const int kn = dec_row_stride<DH, STRIDED>(st, kDK), vn = dec_row_stride<DH, STRIDED>(st, kDV);
     for (int base = k0; base < k1; base += BLK) {
         u32x4 kr[ROUNDS], vr[ROUNDS];
 #pragma unroll
@@ -152,8 +195,8 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             const int j = base + r * RPW + grp;
             kr[r] = vr[r] = u32x4{0u, 0u, 0u, 0u};
             if (j < k1 && has_cols) {
-                kr[r] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)j * DH);
-                vr[r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)j * DH);
+                kr[r] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)j * kn);
+                vr[r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)j * vn);
             }
         }
         // Scores of the block's rows (identical in all G lanes of a group).
@@ -166,8 +209,8 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 float x = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x = __builtin_fmaf(qf[qi][2 * e], bf16_lo(kr[r][e]), x);
-                    x = __builtin_fmaf(qf[qi][2 * e + 1], bf16_hi(kr[r][e]), x);
+                    x = __builtin_fmaf(qf[qi][2 * e], elem_lo<E>(kr[r][e]), x);
+                    x = __builtin_fmaf(qf[qi][2 * e + 1], elem_hi<E>(kr[r][e]), x);
                 }
                 x = group_sum<G>(x);
                 const bool hidden = j >= k1 || (CAUSAL && j > Nk - Nq + qbase + qi);
@@ -193,8 +236,8 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 ps += p;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    add[2 * e] = __builtin_fmaf(p, bf16_lo(vr[r][e]), add[2 * e]);
-                    add[2 * e + 1] = __builtin_fmaf(p, bf16_hi(vr[r][e]), add[2 * e + 1]);
+                    add[2 * e] = __builtin_fmaf(p, elem_lo<E>(vr[r][e]), add[2 * e]);
+                    add[2 * e + 1] = __builtin_fmaf(p, elem_hi<E>(vr[r][e]), add[2 * e + 1]);
                 }
             }
             l[qi] = l[qi] * alpha + ps;
@@ -256,6 +299,13 @@ decode_split_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 // both read patterns).
 constexpr int kDecodeValuQueries = 2;  // at most this many queries: VALU kernel
 constexpr int kDecTile = 32;           // keys per LDS tile
+// Largest half-row probability sum accepted against the current exponent
+// base (every probability of the tile is then at most this): 2^32 for bf16
+// probabilities, 2^15 for fp16 ones (largest finite value 65504).
+template <typename E>
+constexpr float kDecSumMax = 4294967296.f;
+template <>
+constexpr float kDecSumMax<_Float16> = 32768.f;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]); a counter not waited for is set to its maximum.
@@ -267,20 +317,26 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // u*1024 + 16*lane and fetches the global offset src[u] (row and swizzled
 // chunk).  (A function of its own: a buffer descriptor local to a lambda
 // makes the host pass drop the kernel's launch stub.)
-template <int DH, int kLoads>
-__device__ __forceinline__ void decode_copy_tile(const __bf16 *Kh, const __bf16 *Vh, int c0, int k1,
+template <int DH, int kLoads, bool STRIDED>
+__device__ __forceinline__ void decode_copy_tile(const void *Kh, const void *Vh, int c0, int k1,
                                                  LDS3 char *kd, LDS3 char *vd,
-                                                 const uint32_t *src) {
-    const uint32_t bytes = __builtin_amdgcn_readfirstlane(
-        (uint32_t)max(0, min(kDecTile, k1 - c0)) * (uint32_t)(DH * 2));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)c0 * DH, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)c0 * DH, bytes);
+                                                 const uint32_t *ksrc, const uint32_t *vsrc,
+                                                 int kn, int vn) {
+    const uint32_t rows = (uint32_t)max(0, min(kDecTile, k1 - c0));
+    const uint32_t kbytes = __builtin_amdgcn_readfirstlane(
+        STRIDED ? (rows ? (rows - 1) * (uint32_t)kn * 2u + DH * 2u : 0u) : rows * (uint32_t)(DH * 2));
+    const uint32_t vbytes = __builtin_amdgcn_readfirstlane(
+        STRIDED ? (rows ? (rows - 1) * (uint32_t)vn * 2u + DH * 2u : 0u) : rows * (uint32_t)(DH * 2));
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc((const char *)Kh + (size_t)c0 * (size_t)kn * 2, kbytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc((const char *)Vh + (size_t)c0 * (size_t)vn * 2, vbytes);
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(kd + u * 1024), 16, src[u], 0, 0,
-                                                 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(vd + u * 1024), 16, src[u], 0, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS3 void *)(kd + u * 1024), 16, ksrc[u], 0,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS3 void *)(vd + u * 1024), 16, vsrc[u], 0,
+                                                 0, 0);
     }
 }
 
@@ -293,13 +349,13 @@ __device__ __forceinline__ void decode_copy_tile(const __bf16 *Kh, const __bf16 
 // are gathered at the DH row stride (the columns at and past DH hold the
 // next row's leading elements, or zeros past the tile, and feed only the
 // O^T rows at and past DH), and the first DH columns are stored.
-template <int DH, bool CAUSAL>
+template <typename E, int DH, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(kDecLayout<DH> == 64 ? 2 : 1)))
-decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-                   const __bf16 *__restrict__ V, float *__restrict__ o_part,
-                   float *__restrict__ lse_part, int Nq, int Nk, int S, int chunk, float scale,
-                   float scale_log2) {
+decode_mfma_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+                   float *__restrict__ o_part, float *__restrict__ lse_part, int Nq, int Nk,
+                   int S, int chunk, float scale, float scale_log2, DecStrides st) {
+    typedef typename TileOps<E>::x8 X8;
     constexpr int D = kDecLayout<DH>;
     constexpr int KS = DH / 16;                // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;                 // 32-wide d blocks of O^T
@@ -324,12 +380,14 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
     // Q^T as the B operand: lane (g, j) holds query j (zero past Nq),
     // columns 16ks + 8g .. +7.
-    bf16x8 qop[KS];
+    X8 qop[KS];
+    const E *Qr = Q + dec_head_offset<DH, STRIDED>(st, bh, Nq, kDQ) +
+                  (size_t)j * dec_row_stride<DH, STRIDED>(st, kDQ);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (j < Nq) x = load16(Q + ((size_t)bh * Nq + j) * DH + 16 * ks + 8 * g);
-        qop[ks] = __builtin_bit_cast(bf16x8, x);
+        if (j < Nq) x = load16(Qr + 16 * ks + 8 * g);
+        qop[ks] = __builtin_bit_cast(X8, x);
     }
     // Query j sees keys up to vis (below the chunk's end; under the mask,
     // keys <= Nk - Nq + j).
@@ -339,17 +397,24 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     // Tile copies: load u fills LDS chunk positions u*64 + lane, i.e. row
     // u*kRowsPerLoad + lane / (D/8), stored chunk lane % (D/8), and fetches the
     // logical chunk the swizzle stores there.
-    uint32_t src[kLoads];
+    // A position whose logical chunk lies at or past DH/8 fetches chunk
+    // c mod DH/8 of the same row (every byte read belongs to a row).
+    const int kn = dec_row_stride<DH, STRIDED>(st, kDK), vn = dec_row_stride<DH, STRIDED>(st, kDV);
+    uint32_t ksrc[kLoads], vsrc[kLoads];
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
         const int r = u * kRowsPerLoad + lane / (D / 8);
         const int p = lane % (D / 8);
-        src[u] = (uint32_t)(r * DH * 2 + ((p ^ swz<D>(r)) << 4));
+        int c = p ^ swz<D>(r);
+        if (DH < D) c %= DH / 8;
+        ksrc[u] = (uint32_t)(r * kn * 2 + (c << 4));
+        vsrc[u] = STRIDED ? (uint32_t)(r * vn * 2 + (c << 4)) : ksrc[u];
     }
-    const __bf16 *Kh = K + (size_t)bh * Nk * DH;
-    const __bf16 *Vh = V + (size_t)bh * Nk * DH;
+    const E *Kh = K + dec_head_offset<DH, STRIDED>(st, bh, Nk, kDK);
+    const E *Vh = V + dec_head_offset<DH, STRIDED>(st, bh, Nk, kDV);
     auto copy_tile = [&](int t, LDS3 char *kd, LDS3 char *vd) __attribute__((always_inline)) {
-        decode_copy_tile<DH, kLoads>(Kh, Vh, k0 + t * kDecTile, k1, kd, vd, src);
+        decode_copy_tile<DH, kLoads, STRIDED>(Kh, Vh, k0 + t * kDecTile, k1, kd, vd, ksrc, vsrc,
+                                              kn, vn);
     };
     static_assert(kLoads * 1024 == kTileBytes, "tile copy");
 
@@ -366,7 +431,7 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
     // Probabilities of the tile's 32 keys against base mcx (scaled log2
     // units) as P^T operands (keys 0-15, 16-31), and their half-wave sum.
-    auto exps = [&](const f32x16 &sc, float mcx, bf16x8 (&p)[2]) __attribute__((always_inline)) {
+    auto exps = [&](const f32x16 &sc, float mcx, X8 (&p)[2]) __attribute__((always_inline)) {
         f32x8 lo, hi;
         float ra = 0.f, rb = 0.f;
 #pragma unroll
@@ -376,8 +441,8 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             ra += lo[r];
             rb += hi[r];
         }
-        p[0] = __builtin_convertvector(lo, bf16x8);
-        p[1] = __builtin_convertvector(hi, bf16x8);
+        p[0] = __builtin_convertvector(lo, X8);
+        p[1] = __builtin_convertvector(hi, X8);
         return ra + rb;
     };
 
@@ -392,8 +457,8 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const LDS3 bf16x8 *>(kt + row_read_at(rd, ks));
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qop[ks], sc, 0, 0, 0);
+            const X8 kf = *reinterpret_cast<const LDS3 X8 *>(kt + row_read_at(rd, ks));
+            sc = TileOps<E>::mfma(kf, qop[ks], sc);
         }
         // Element r of sc is key c0 + 8(r/4) + 4g + r%4 of query j.
         const int c0 = k0 + t * kDecTile;
@@ -403,9 +468,9 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             for (int r = 0; r < 16; ++r)
                 if (8 * (r >> 2) + (r & 3) > lim) sc[r] = -INFINITY;
         }
-        bf16x8 pp[2];
+        X8 pp[2];
         float rs = exps(sc, mc_run, pp);
-        if (__ballot(!(rs <= 4294967296.f))) {
+        if (__ballot(!(rs <= kDecSumMax<E>))) {
             float mt = sc[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
@@ -432,8 +497,7 @@ decode_mfma_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<D>(vt, trd, tt, db), pp[tt],
-                                                                  acc[db], 0, 0, 0);
+                acc[db] = TileOps<E>::mfma(tr_read<D, X8>(vt, trd, tt, db), pp[tt], acc[db]);
         // every read of these buffers has completed before they are refilled
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         copy_tile(t + 3, kt, vt);
@@ -512,10 +576,10 @@ __device__ __forceinline__ void merge_pair(float &m, float &l, float mo, float l
     m = mn;
 }
 
-template <int DH>
+template <typename E, int DH, bool STRIDED>
 __global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ lse_part,
-                    __bf16 *__restrict__ O, float *__restrict__ LSE, int Nq, int S) {
+                    E *__restrict__ O, float *__restrict__ LSE, int Nq, int S, DecStrides st) {
     // Threads are laid out over D >= DH columns (a divisor of the workgroup
     // size); those of the columns at and past DH add nothing.
     constexpr int D = DH <= 64 ? 64 : 128;
@@ -566,47 +630,74 @@ decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ 
         float o = part[c];
 #pragma unroll
         for (int k = 1; k < kSlices; ++k) o += part[k * D + c];
-        O[(size_t)row * DH + c] = (__bf16)o;
+        O[dec_head_offset<DH, STRIDED>(st, bh, Nq, kDO) +
+          (size_t)qi * dec_row_stride<DH, STRIDED>(st, kDO) + c] = (E)o;
         if (c == 0) LSE[row] = lse;
     }
 }
 
-template <int D, int NQ, bool CAUSAL>
+template <typename E, int DH, int NQ, bool CAUSAL, bool STRIDED>
 hipError_t launch_nq(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                      int H, int Nq, int Nk, int S, int chunk, float scale, float *o_part,
-                     float *lse_part, hipStream_t stream) {
+                     float *lse_part, const DecStrides &st, hipStream_t stream) {
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+    const E *Q = static_cast<const E *>(q), *K = static_cast<const E *>(k),
+            *V = static_cast<const E *>(v);
     if constexpr (NQ > kDecodeValuQueries)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, CAUSAL>), dim3(B * H * S), dim3(64), 0, stream,
-                           static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-                           static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk,
-                           scale, scale_log2);
+        hipLaunchKernelGGL((decode_mfma_kernel<E, DH, CAUSAL, STRIDED>), dim3(B * H * S), dim3(64),
+                           0, stream, Q, K, V, o_part, lse_part, Nq, Nk, S, chunk, scale,
+                           scale_log2, st);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, NQ, CAUSAL>), dim3(B * H * S),
-                           dim3(64 * kDecodeWaves<NQ>), 0, stream,
-                           static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-                           static_cast<const __bf16 *>(v), o_part, lse_part, Nq, Nk, S, chunk,
-                           scale, scale_log2);
+        hipLaunchKernelGGL((decode_split_kernel<E, DH, NQ, CAUSAL, STRIDED>), dim3(B * H * S),
+                           dim3(64 * kDecodeWaves<NQ>), 0, stream, Q, K, V, o_part, lse_part, Nq,
+                           Nk, S, chunk, scale, scale_log2, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(B * H * Nq), dim3(kMergeThreads), 0, stream,
-                       o_part, lse_part, static_cast<__bf16 *>(o), lse, Nq, S);
+    hipLaunchKernelGGL((decode_merge_kernel<E, DH, STRIDED>), dim3(B * H * Nq),
+                       dim3(kMergeThreads), 0, stream, o_part, lse_part, static_cast<E *>(o), lse,
+                       Nq, S, st);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_d(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                    int Nq, int Nk, int S, int chunk, float scale, float *o_part, float *lse_part,
-                    hipStream_t stream) {
-#define FA_DECODE_NQ(NQ)                                                                      \
-    return launch_nq<D, NQ, CAUSAL>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,  \
-                                    lse_part, stream)
+template <typename E, int DH, bool CAUSAL, bool STRIDED>
+hipError_t launch_q(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int H, int Nq, int Nk, int S, int chunk, float scale, float *o_part,
+                    float *lse_part, const DecStrides &st, hipStream_t stream) {
+#define FA_DECODE_NQ(NQ)                                                                        \
+    return launch_nq<E, DH, NQ, CAUSAL, STRIDED>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, \
+                                                 o_part, lse_part, st, stream)
     if (Nq <= 1) FA_DECODE_NQ(1);
     if (Nq <= 2) FA_DECODE_NQ(2);
-    if (Nq <= 4) FA_DECODE_NQ(4);
-    if (Nq <= 8) FA_DECODE_NQ(8);
+    // From three queries on the MFMA kernel runs, whatever the count.
     FA_DECODE_NQ(16);
 #undef FA_DECODE_NQ
+}
+
+template <typename E, bool STRIDED>
+hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int H, int Nq, int Nk, int d, float scale, bool causal, int S, float *o_part,
+                    float *lse_part, const DecStrides &st, hipStream_t stream) {
+    const int chunk = decode_chunk(Nk, S);
+    S = (Nk + chunk - 1) / chunk;  // no empty chunk
+#define FA_DEC_CASE(DH)                                                                         \
+    case DH:                                                                                    \
+        return causal ? launch_q<E, DH, true, STRIDED>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, \
+                                                       scale, o_part, lse_part, st, stream)    \
+                      : launch_q<E, DH, false, STRIDED>(q, k, v, o, lse, B, H, Nq, Nk, S,       \
+                                                        chunk, scale, o_part, lse_part, st,     \
+                                                        stream)
+    switch (d) {
+        FA_DEC_CASE(16);
+        FA_DEC_CASE(32);
+        FA_DEC_CASE(48);
+        FA_DEC_CASE(64);
+        FA_DEC_CASE(80);
+        FA_DEC_CASE(96);
+        FA_DEC_CASE(112);
+        FA_DEC_CASE(128);
+        default: return hipErrorInvalidValue;
+    }
+#undef FA_DEC_CASE
 }
 
 }  // namespace
@@ -632,29 +723,35 @@ int decode_chunk(int Nk, int S) {
 hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                               int B, int H, int Nq, int Nk, int d, float scale, bool causal,
                               int S, float *o_part, float *lse_part, hipStream_t stream) {
-    const int chunk = decode_chunk(Nk, S);
-    S = (Nk + chunk - 1) / chunk;  // no empty chunk
-#define FA_DEC_CASE(DH)                                                                          \
-    case DH:                                                                                     \
-        return causal ? launch_d<DH, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale, o_part,  \
-                                           lse_part, stream)                                     \
-                      : launch_d<DH, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale,         \
-                                            o_part, lse_part, stream)
-    switch (d) {
-        FA_DEC_CASE(16);
-        FA_DEC_CASE(32);
-        FA_DEC_CASE(48);
-        FA_DEC_CASE(64);
-        FA_DEC_CASE(80);
-        FA_DEC_CASE(96);
-        FA_DEC_CASE(112);
-        default:
-            return causal ? launch_d<128, true>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale,
-                                                o_part, lse_part, stream)
-                          : launch_d<128, false>(q, k, v, o, lse, B, H, Nq, Nk, S, chunk, scale,
-                                                 o_part, lse_part, stream);
+    const DecStrides none = {};
+    return launch_e<__bf16, false>(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, S, o_part,
+                                   lse_part, none, stream);
+}
+
+hipError_t launch_decode_ex(bool fp16, const void *q, const void *k, const void *v, void *o,
+                            float *lse, int B, int H, int Nq, int Nk, int d, float scale,
+                            bool causal, int S, float *o_part, float *lse_part,
+                            const int64_t *strides, hipStream_t stream) {
+    DecStrides st;
+    bool dense = true;
+    for (int t = 0; t < kDecTensors; ++t) {
+        const int64_t *x = strides + 3 * t;
+        const long long rows = (t == kDQ || t == kDO) ? Nq : Nk;
+        dense = dense && x[0] == (long long)H * rows * d && x[1] == rows * d && x[2] == d;
+        st.b[t] = x[0];
+        st.h[t] = x[1];
+        st.n[t] = (int)x[2];
     }
-#undef FA_DEC_CASE
+    st.H = H;
+    if (fp16)
+        return dense ? launch_e<_Float16, false>(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, S,
+                                                 o_part, lse_part, st, stream)
+                     : launch_e<_Float16, true>(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, S,
+                                                o_part, lse_part, st, stream);
+    return dense ? launch_e<__bf16, false>(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, S,
+                                           o_part, lse_part, st, stream)
+                 : launch_e<__bf16, true>(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, S,
+                                          o_part, lse_part, st, stream);
 }
 
 }  // namespace fa

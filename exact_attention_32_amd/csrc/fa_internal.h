@@ -59,5 +59,12 @@ int decode_chunk(int Nk, int S);
 hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                               int B, int H, int Nq, int Nk, int d, float scale, bool causal,
                               int S, float *o_part, float *lse_part, hipStream_t stream);
+// The same on bf16 (fp16 = false) or fp16 views with element strides (q, k,
+// v, o: batch, head, row; d contiguous); the dense layout takes the
+// contiguous kernels.
+hipError_t launch_decode_ex(bool fp16, const void *q, const void *k, const void *v, void *o,
+                            float *lse, int B, int H, int Nq, int Nk, int d, float scale,
+                            bool causal, int S, float *o_part, float *lse_part,
+                            const int64_t *strides, hipStream_t stream);
 
 }  // namespace fa

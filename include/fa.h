@@ -169,6 +169,30 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
 
 /*
+ * fa_decode_ex -- fa_decode generalised the way fa_fwd_ex generalises
+ * fa_fwd: fp16 as well as bf16 tensors, and strided views (the Triton page's
+ * kernel interface, "手写 FlashAttention", section 3.4), e.g. a key/value
+ * cache kept as [B, Nk, H, d].
+ *
+ *   dtype   : FA_DTYPE_BF16 or FA_DTYPE_FP16 -- the type of q, k, v and o
+ *             (scores, statistics and sums fp32; with three or more queries
+ *             the products run on that type's MFMA and the probabilities
+ *             are rounded to it; o rounded to nearest even)
+ *   strides : host array of 12 element strides, for q, k, v, o in turn:
+ *             batch, head, row (q and o have Nq rows, k and v Nk), with the
+ *             rules of fa_fwd_ex; lse stays a dense fp32 [B, H, Nq] and the
+ *             workspace is fa_decode_workspace_size(...) bytes as for
+ *             fa_decode.
+ * Other arguments, ownership and errors as for fa_decode, plus FA_ERR_DTYPE
+ * and FA_ERR_STRIDE.  With the dense strides and dtype bf16 this runs
+ * exactly fa_decode's kernels.
+ */
+int fa_decode_ex(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                 void *workspace, size_t workspace_bytes, const int64_t *strides,
+                 hipStream_t stream);
+
+/*
  * fa_fwd_ex -- fa_fwd generalised to fp16 as well as bf16 tensors, and to
  * strided views, as the Triton page's kernel takes per-tensor strides
  * ("手写 FlashAttention", section 3.4, its kernel's parameter list).

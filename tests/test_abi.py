@@ -257,3 +257,30 @@ def test_bwd_ex_validation_codes(lib):
     assert call(strides=bshd, delta=BL + 64) == fa.FA_ERR_ALIAS
     assert call(strides=bshd, dv=BDQ + 128) == fa.FA_ERR_ALIAS   # outputs overlap
     assert call(strides=bshd, q=BQ + 8) == fa.FA_ERR_ALIGN
+
+
+def test_decode_ex_validation_codes(lib):
+    B, H, Nq, Nk, d = 2, 3, 4, 500, 64
+    dense = [H * Nq * d, Nq * d, d, H * Nk * d, Nk * d, d, H * Nk * d, Nk * d, d,
+             H * Nq * d, Nq * d, d]
+    DQ, DK, DV, DO, DL, DW = (BASE + i * GAP for i in range(6))
+
+    def call(dtype=fa.FA_DTYPE_BF16, strides=dense, **kw):
+        p = dict(q=DQ, k=DK, v=DV, o=DO, lse=DL, ws=DW, wsb=1 << 30)
+        p.update(kw)
+        return fa.fa_decode_ex(dtype, p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, Nq, Nk, d,
+                               0.125, 1, 0, p["ws"], p["wsb"], strides, None)
+    assert call(strides=None) == fa.FA_ERR_NULL
+    assert call(o=0) == fa.FA_ERR_NULL
+    assert call(dtype=5) == fa.FA_ERR_DTYPE
+    bad = list(dense); bad[5] = 32                  # k row stride < d
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    bad = list(dense); bad[4] = Nk * d + 4          # k head stride not a multiple of 8
+    assert call(strides=bad) == fa.FA_ERR_ALIGN
+    bad = list(dense); bad[9:12] = [H * Nq * d, 2 * d, d]   # o heads overlap
+    assert call(strides=bad) == fa.FA_ERR_STRIDE
+    assert call(wsb=64) == fa.FA_ERR_WORKSPACE
+    assert call(ws=DK) == fa.FA_ERR_ALIAS
+    assert call(o=DV + 64) == fa.FA_ERR_ALIAS
+    shared = list(dense); shared[3:5] = [Nk * d, 0]          # k shared by all heads: allowed
+    assert call(strides=shared, o=DQ) == fa.FA_ERR_ALIAS     # (fails on the alias only)
