@@ -177,10 +177,25 @@ __device__ __forceinline__ int k_logical(int r, int p) {
 constexpr uint32_t kNoChunk = 0xFFFFFFF0u;
 
 // Workgroup id -> (batch*head, query tile).  Consecutive ids go to
-// consecutive XCDs; when the grid divides evenly, XCD x receives the
-// contiguous range [x*W/8, (x+1)*W/8) of (head, tile) pairs.
-__device__ __forceinline__ void map_block(int L, int W, int nqt, bool heavy_first,
-                                          int &bh, int &qt) {
+// consecutive XCDs.
+//  * Tiles of equal cost (no mask): when the grid divides evenly, XCD x
+//    receives the contiguous range [x*W/8, (x+1)*W/8) of (head, tile) pairs,
+//    so that its L2 serves one head's stream at a time.
+//  * Causal (a tile's cost grows with its index): ids in order of decreasing
+//    cost, one cost rank after the other over all heads -- largest first, so
+//    that the cheap tiles fill the gaps left at the end of the grid (a
+//    makespan measured 25 % shorter at B16 H12 N1000 d64, 2 % at B2 H32
+//    N8192 d128).  With a head count that is a multiple of 8, id mod 8 =
+//    head mod 8: every tile of a head still runs on one XCD.
+__device__ __forceinline__ void map_block(int L, int W, int nqt, bool causal, int &bh,
+                                          int &qt) {
+    if (causal) {
+        const int heads = W / nqt;
+        const int rank = L / heads;
+        bh = L - rank * heads;
+        qt = nqt - 1 - rank;
+        return;
+    }
     int gidx = L;
     if ((W & 7) == 0) {
         const int per = W >> 3;
@@ -188,7 +203,6 @@ __device__ __forceinline__ void map_block(int L, int W, int nqt, bool heavy_firs
     }
     bh = gidx / nqt;
     qt = gidx - bh * nqt;
-    if (heavy_first) qt = nqt - 1 - qt;
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) {
