@@ -178,18 +178,23 @@ constexpr uint32_t kNoChunk = 0xFFFFFFF0u;
 
 // Workgroup id -> (batch*head, query tile).  Consecutive ids go to
 // consecutive XCDs.
-//  * Tiles of equal cost (no mask): when the grid divides evenly, XCD x
-//    receives the contiguous range [x*W/8, (x+1)*W/8) of (head, tile) pairs,
-//    so that its L2 serves one head's stream at a time.
-//  * Causal (a tile's cost grows with its index): ids in order of decreasing
-//    cost, one cost rank after the other over all heads -- largest first, so
-//    that the cheap tiles fill the gaps left at the end of the grid (a
-//    makespan measured 25 % shorter at B16 H12 N1000 d64, 2 % at B2 H32
-//    N8192 d128).  With a head count that is a multiple of 8, id mod 8 =
-//    head mod 8: every tile of a head still runs on one XCD.
-__device__ __forceinline__ void map_block(int L, int W, int nqt, bool causal, int &bh,
-                                          int &qt) {
-    if (causal) {
+//  * By default, when the grid divides evenly, XCD x receives the contiguous
+//    range [x*W/8, (x+1)*W/8) of (head, tile) pairs, heavy tiles first
+//    within a head under the causal mask: the XCD works through its heads
+//    about one at a time and its L2 serves that head's K/V stream.
+//  * Causal with fewer query tiles per head than `by_cost_below` (about
+//    the workgroup slots of one XCD, so that many heads are in flight on an
+//    XCD anyway): ids in order of decreasing cost, one cost rank after the
+//    other over all heads -- largest first, so that the cheap tiles fill the
+//    gaps left at the end of the grid (a makespan 22 % shorter at B16 H12
+//    N1000 d64).  With a head count that is a multiple of 8, id mod 8 =
+//    head mod 8: every tile of a head still runs on one XCD.  With long
+//    rows this order measured 1 % faster at B2 H32 N8192 d128 but fetched
+//    2.2x the HBM bytes (every head's K/V in flight at once), so long rows
+//    keep the contiguous order.
+__device__ __forceinline__ void map_block(int L, int W, int nqt, bool causal, int by_cost_below,
+                                          int &bh, int &qt) {
+    if (causal && nqt < by_cost_below) {
         const int heads = W / nqt;
         const int rank = L / heads;
         bh = L - rank * heads;
@@ -203,6 +208,7 @@ __device__ __forceinline__ void map_block(int L, int W, int nqt, bool causal, in
     }
     bh = gidx / nqt;
     qt = gidx - bh * nqt;
+    if (causal) qt = nqt - 1 - qt;
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) {
@@ -294,7 +300,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     const int j = lane & 31;  // query column of this lane (S^T / O^T layouts)
 
     int bh, qt;
-    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
+    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, 64, bh, qt);  // 2-3 workgroups per CU
     const int r0 = qt * kBr;
     size_t qoff, koff, voff, ooff;
     int qn, kn, vn, on;
@@ -671,7 +677,7 @@ fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
     const int j = lane & 31;
 
     int bh, qt;
-    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, bh, qt);
+    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, 32 * (8 / W), bh, qt);  // 8 / W per CU
     const int r0 = qt * kRows;
     size_t qoff, koff, voff, ooff;
     int qn, kn, vn, on;
