@@ -116,7 +116,7 @@ bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restr
     const int j = lane & 31;
 
     int bh, qt;
-    map_block(blockIdx.x, gridDim.x, ntiles, CAUSAL, bh, qt);
+    map_block(blockIdx.x, gridDim.x, ntiles, CAUSAL, CAUSAL, 64, bh, qt);  // 2 per CU
     const int r0 = qt * kOuter;
     const E *Kh = K + head_offset<DH, STRIDED>(st, bh, N, kTK);
     const E *Vh = V + head_offset<DH, STRIDED>(st, bh, N, kTV);
@@ -288,7 +288,7 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
     int bh, kt;
     // Under the causal mask the first key tiles see the most queries: they
     // are issued first (no reversal).
-    map_block(blockIdx.x, gridDim.x, ntiles, false, bh, kt);
+    map_block(blockIdx.x, gridDim.x, ntiles, false, CAUSAL, 64, bh, kt);  // 2 per CU
     const int k0 = kt * kOuter;
     const E *Qh = Q + head_offset<DH, STRIDED>(st, bh, N, kTQ);
     const E *dOh = dO + head_offset<DH, STRIDED>(st, bh, N, kTDO);

@@ -69,11 +69,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
-// Workgroup id -> (batch*head, tile): consecutive ids go to consecutive XCDs,
-// and XCD x walks the contiguous range [x*W/8, (x+1)*W/8) of (head, tile)
-// pairs when the grid divides evenly (its L2 then serves one head's stream).
-__device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse, int &bh,
-                                          int &tile) {
+// Workgroup id -> (batch*head, tile): consecutive ids go to consecutive XCDs.
+// By default XCD x walks the contiguous range [x*W/8, (x+1)*W/8) of (head,
+// tile) pairs when the grid divides evenly (its L2 then serves one head's
+// stream).  With `by_cost` (causal: a tile's cost grows with its index, or
+// falls with it when `reverse`) and fewer than `by_cost_below` tiles per
+// head, ids go in order of decreasing cost, one cost rank after the other
+// over all heads (largest first, so that cheap tiles fill the gaps at the
+// end of the grid); with a head count that is a multiple of 8, id mod 8 =
+// head mod 8, so every tile of a head still runs on one XCD.
+__device__ __forceinline__ void map_block(int L, int W, int ntiles, bool reverse, bool by_cost,
+                                          int by_cost_below, int &bh, int &tile) {
+    if (by_cost && ntiles < by_cost_below) {
+        const int heads = W / ntiles;
+        const int rank = L / heads;
+        bh = L - rank * heads;
+        tile = reverse ? ntiles - 1 - rank : rank;
+        return;
+    }
     int gidx = L;
     if ((W & 7) == 0) gidx = (L & 7) * (W >> 3) + (L >> 3);
     bh = gidx / ntiles;
