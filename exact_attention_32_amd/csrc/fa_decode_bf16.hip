@@ -554,7 +554,7 @@ decode_mfma_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__
 //     into a (max, sum) pair; the pairs are merged across the workgroup.
 //  2. O = sum_s e^(LSE_s - LSE) O_s: the weights of up to kMergeChunk chunks
 //     at a time go to LDS; thread t adds column t % D of the chunks
-//     s = t / D (mod 256 / D), with independent loads; the 256 / D slices
+//     s = t / D (mod 256 / D), eight loads in flight per thread; the 256 / D slices
 //     are summed through LDS at the end.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeChunk = 1024;
@@ -608,7 +608,12 @@ decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ 
     const float lse = m + logf(l);
 
     const int c = t % D, slice = t / D;
-    float acc0 = 0.f, acc1 = 0.f;
+    // Eight independent partial sums per thread, so that eight loads of
+    // partial rows are in flight at once (the loop is bound by their latency).
+    constexpr int kAcc = 8;
+    float acc[kAcc];
+#pragma unroll
+    for (int u = 0; u < kAcc; ++u) acc[u] = 0.f;
     for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
         const int n = min(kMergeChunk, S - s0);
         __syncthreads();  // the previous chunk's weights are no longer read
@@ -618,13 +623,18 @@ decode_merge_kernel(const float *__restrict__ o_part, const float *__restrict__ 
         const float *op = o_part + (((size_t)bh * S + s0) * Nq + qi) * DH + c;
         const size_t stride = (size_t)Nq * DH;
         int s = c < DH ? slice : n;
-        for (; s + kSlices < n; s += 2 * kSlices) {
-            acc0 = __builtin_fmaf(wts[s], op[(size_t)s * stride], acc0);
-            acc1 = __builtin_fmaf(wts[s + kSlices], op[(size_t)(s + kSlices) * stride], acc1);
+        for (; s + (kAcc - 1) * kSlices < n; s += kAcc * kSlices) {
+#pragma unroll
+            for (int u = 0; u < kAcc; ++u)
+                acc[u] = __builtin_fmaf(wts[s + u * kSlices], op[(size_t)(s + u * kSlices) * stride],
+                                        acc[u]);
         }
-        if (s < n) acc0 = __builtin_fmaf(wts[s], op[(size_t)s * stride], acc0);
+        for (; s < n; s += kSlices) acc[0] = __builtin_fmaf(wts[s], op[(size_t)s * stride], acc[0]);
     }
-    part[t] = acc0 + acc1;
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kAcc; ++u) sum += acc[u];
+    part[t] = sum;
     __syncthreads();
     if (slice == 0 && c < DH) {
         float o = part[c];
