@@ -14,9 +14,10 @@
 // states both orders give the same result.
 //
 // Two kernels share the operand layouts, LDS swizzles, softmax and grid
-// mapping described here: fwd_kernel (the head dims other than 128) and
-// fwd_pipe_kernel (head dim 128), which reorders the work inside a wave
-// into a software pipeline and runs 8-wave workgroups; see its own comment
+// mapping described here: fwd_kernel (every head dim but 128, except causal
+// d = 64 on long rows) and fwd_pipe_kernel (head dim 128 with 8-wave
+// workgroups; causal d = 64 with N >= 8192 with 4-wave ones), which reorders
+// the work inside a wave into a software pipeline; see its own comment
 // further down.
 //
 // Mapping onto CDNA4 (described for fwd_kernel at d = 128; d/16 k-steps and
@@ -25,8 +26,9 @@
 // ------------------
 // * One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
 //   wave owns 32 rows for the whole key loop (Q, the output accumulator and
-//   the running max / sum never leave registers).  Two workgroups share a
-//   compute unit, i.e. each SIMD runs one wave of each.
+//   the running max / sum never leave registers).  Two workgroups (three
+//   at d <= 64, where a wave needs at most 168 registers) share a compute
+//   unit, each SIMD running one wave of each.
 // * Key/value tiles of 64 keys are copied global -> LDS by buffer loads that
 //   write LDS directly (no registers; rows past N arrive as zeros), double
 //   buffered.  The loads of tile t+1 are spread over the S MFMAs of tile t
