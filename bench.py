@@ -425,7 +425,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py: this build measures one GPU only (single-GPU kernel, no "
+            print("bench.py: the library runs on one GPU (single-GPU kernels, no "
                   "collectives); run it with --gpus 1.", flush=True)
         return 2
 
