@@ -12,16 +12,15 @@
 // body does for (i, j):
 //   load K_j, V_j (direct-to-LDS) and Q_i;
 //   S_ij = Q_i K_j^T (computed as S^T = K Q^T on v_mfma_f32_32x32x16_bf16);
-//   m~ = rowmax(S_ij), P~ = exp(S_ij - m~), l~ = rowsum(P~)      (line 10)
-//   m_new = max(m_i, m~), l_new = e^(m_i - m_new) l_i + e^(m~ - m_new) l~
-//                                                                  (line 11)
-//   O_i <- (l_i e^(m_i - m_new) O_i + e^(m~ - m_new) P~ V_j) / l_new
-//                                                                  (line 12)
-//   write O_i, l_i = l_new, m_i = m_new back                       (line 13)
+//   block statistics: m~ = rowmax(S_ij), P~ = exp(S_ij - m~), l~ = rowsum(P~);
+//   merged statistics: m_new = max(m_i, m~),
+//     l_new = e^(m_i - m_new) l_i + e^(m~ - m_new) l~;
+//   rescaled output: O_i <- (l_i e^(m_i - m_new) O_i + e^(m~ - m_new) P~ V_j) / l_new;
+//   write O_i, l_i = l_new, m_i = m_new back.
 // O_i, l_i, m_i live in an fp32 workspace (rounding O to bf16 after every
 // step would add one rounding per key block).  The first step of a row block
-// starts from O = 0, l = 0, m = -inf (line 2) without reading the workspace;
-// the last step that touches a row block writes the bf16 output and
+// starts from the algorithm's initial O = 0, l = 0, m = -inf without reading
+// the workspace; the last step that touches a row block writes the bf16 output and
 // LSE = m*scale + ln(l) instead of the state.  Under the causal mask a
 // launch j covers only the row blocks that can see a key of block j.
 #include <hip/hip_runtime.h>
@@ -66,12 +65,12 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const bool valid = qrow < N;
     const int c0 = j * kInner;
 
-    // line 6: K_j, V_j to on-chip memory
+    // K_j, V_j to on-chip memory
     const uint32_t src = tile_src_offset<D, DH>(wave, lane);
     load_tile<D, DH>(K + hoff, N, c0, (LDS3 char *)lds_k, src, wave);
     load_tile<D, DH>(V + hoff, N, c0, (LDS3 char *)lds_v, src, wave);
 
-    // line 8: Q_i (as the B operand of S^T = K Q^T) and the row state
+    // Q_i (as the B operand of S^T = K Q^T) and the row state
     bf16x8 qop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -109,7 +108,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // line 9: S^T = K_j Q_i^T (element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4)
+    // S^T = K_j Q_i^T (element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4)
     f32x16 s[kInner / 32];
 #pragma unroll
     for (int kb = 0; kb < kInner / 32; ++kb)
@@ -134,7 +133,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                 if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
     }
 
-    // line 10: block statistics with the block's own maximum
+    // block statistics with the block's own maximum
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < kInner / 32; ++kb)
@@ -180,7 +179,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
             pv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 tr_read<D>((const LDS3 char *)lds_v, trd, T, db), pop[T], pv[db], 0, 0, 0);
 
-    // lines 11-12: merge with the stored state (a block with no visible key
+    // merge with the stored state (a block with no visible key
     // for this row leaves it unchanged)
     const float m_new = fmaxf(m_i, mt);
     const float a_old = m_i == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_i - m_new) * scale_log2);
@@ -199,7 +198,7 @@ kvouter_step_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         store_rows<D, DH>(O + hoff + (size_t)qrow * DH, o_i, 1.f, g);
         if (g == 0) LSE[(size_t)bh * N + qrow] = m_new * scale + logf(l_new);
     } else {
-        // line 13: the state back to device memory
+        // the state back to device memory
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll

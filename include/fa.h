@@ -248,16 +248,16 @@ int fa_bwd_ex(int dtype, const void *q, const void *k, const void *v, const void
  * the loop order of Algorithm 1 of "解析 FlashAttention（2）：FlashAttention-v1
  * 前向传播" (section 4): key/value blocks outside, query blocks inside, the
  * output O and the statistics l, m written back to device memory after every
- * step (lines 12-13) and read again at the next one (line 8).  It exists to
+ * step and read again at the next one.  It exists to
  * measure that order against fa_fwd's (query blocks outside, which the
  * unit-12 loop-order lesson of "在线 Softmax 与 FlashAttention" shows gives
  * the same O without those round trips).
  *
  * One kernel launch per 64-key block j is enqueued on `stream`; each covers
  * the 128-row query blocks that can see block j.  Per (i, j) it computes the
- * block statistics with the block's own maximum (line 10), merges them with
- * the stored ones (line 11) and rescales the stored, normalised O_i
- * (line 12).  The state O, l, m is fp32 in the caller's workspace (at least
+ * block statistics with the block's own maximum, merges them with the
+ * stored ones and rescales the stored, normalised O_i, as the algorithm's
+ * inner step does.  The state O, l, m is fp32 in the caller's workspace (at least
  * fa_fwd_kv_outer_workspace_size bytes; contents on return unspecified; no
  * overlap with any other argument).  Arguments, shapes and errors otherwise
  * as for fa_fwd, plus FA_ERR_WORKSPACE.
