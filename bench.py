@@ -32,6 +32,11 @@ peak; `traffic` comes from the committed rocprofv3 counter summary of the
 same command when it still matches the kernel source.  `cpu_baseline` times
 the fp64 oracle on a bounded sample of rows of the same workload.
 
+`python bench.py --oracle-timings` times the oracle alone (no GPU) on the
+small workloads (fp32 B1 H1 N256 d64; B4 H16 N2048 d64; B16 H12 N1000 d64
+with and without the mask), whole workload, on one core and on every host
+thread, and prints the host's CPU model.
+
 Counter helpers (used to produce the summaries under profiles/):
   python bench.py --copy-calibration ...   also runs one plain device copy
                                            of 1 GiB (for counter scaling)
@@ -105,6 +110,62 @@ def read_traffic(workload: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+ORACLE_TIMING_WORKLOADS = ["w1_f32_n256_d64", "w2_bf16_b4h16_n2048_d64",
+                           "w5a_bf16_b16h12_n1000_d64", "w5b_bf16_b16h12_n1000_d64_causal"]
+
+
+def oracle_timing_child(name: str) -> None:
+    """Time the oracle's full forward pass (every row, the plain definition)
+    on one workload with the OpenMP thread count this process was started
+    with; print one JSON line."""
+    import oracle
+    from exact_attention_32_amd import inputs
+
+    w = inputs.WORKLOADS[name]
+    q, k, v = inputs.make_qkv(w)
+    o = oracle.default()
+    o.attention(q[:, :1, :8], k[:, :1, :8], v[:, :1, :8], w.scale, w.causal)  # warm-up
+    t0 = time.perf_counter()
+    o.attention(q, k, v, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"workload": name, "threads": o.num_threads(), "seconds": round(dt, 3),
+                      "gflops": round(w.flops / dt / 1e9, 3)}), flush=True)
+
+
+def oracle_timings() -> int:
+    """The oracle on the small workloads, on one core and on every host
+    thread, each in a child process (the OpenMP thread count is fixed at
+    start-up).  One JSON line per run, then a summary line."""
+    import subprocess
+
+    rows = []
+    for name in ORACLE_TIMING_WORKLOADS:
+        for threads in ("1", str(os.cpu_count() or 1)):
+            env = dict(os.environ, OMP_NUM_THREADS=threads)
+            r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-timing-child",
+                                name], env=env, capture_output=True, text=True, check=True)
+            line = json.loads(r.stdout.strip().splitlines()[-1])
+            print(json.dumps(line), flush=True)
+            rows.append(line)
+    print(json.dumps({"oracle_timings": rows, "cpu_model": cpu_model(),
+                      "host_threads": os.cpu_count()}), flush=True)
+    return 0
+
+
 def cpu_baseline_bwd(w, q, k, v, dout, target_s: float):
     """The oracle's backward pass timed on the host cores on a seeded sample
     of dQ rows of the same workload.  For each row the oracle forms the
@@ -136,6 +197,7 @@ def cpu_baseline_bwd(w, q, k, v, dout, target_s: float):
         "sample": f"{n} seeded dQ rows of {w.name} (fp64 definition: score, dP and dQ row "
                   f"each), {dt:.1f} s; FLOPs per row = 3/5 of the workload's backward "
                   f"FLOPs / rows",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -168,6 +230,7 @@ def cpu_baseline(w, q, k, v, target_s: float):
         "kind": "oracle",
         "sample": f"{n} seeded output rows of {w.name} (fp64 definition, full score row "
                   f"each), {dt:.1f} s; FLOPs per row = workload FLOPs / rows",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -339,7 +402,8 @@ def bench_decode(args) -> int:
             "value": round(w.bytes / dt / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle",
             "sample": f"the whole workload {reps} time(s), {dt:.2f} s each (fp64 definition "
-                      f"on the same bf16 inputs); bytes = the compulsory bf16 bytes"}
+                      f"on the same bf16 inputs); bytes = the compulsory bf16 bytes",
+            "cpu_model": cpu_model()}
     print(json.dumps(line), flush=True)
     return 0
 
@@ -410,7 +474,17 @@ def main() -> int:
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "WORKLOAD", "COMMAND"))
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG")
+    ap.add_argument("--oracle-timings", action="store_true",
+                    help="time the oracle on the small workloads on one core and on all "
+                         "host threads (no GPU)")
+    ap.add_argument("--oracle-timing-child", metavar="WORKLOAD", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.oracle_timings:
+        return oracle_timings()
+    if args.oracle_timing_child:
+        oracle_timing_child(args.oracle_timing_child)
+        return 0
 
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)

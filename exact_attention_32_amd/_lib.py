@@ -95,6 +95,35 @@ def _stream(s) -> int | None:
     return int(s)
 
 
+def _resolve_stream(stream, device):
+    """The torch stream the work goes to: ``stream`` itself (a torch stream, or
+    a raw HIP stream handle wrapped as an external stream), else the current
+    stream of ``device``.  Buffers the wrappers allocate are allocated while
+    this stream is current, so the caching allocator hands their memory to
+    later allocations on other streams only after this stream's work."""
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _check_out(t, name, shape, dtype, dense=False):
+    """Reject a caller-supplied output the kernels could not write safely:
+    the C ABI sees only its address, so its shape, type, device and layout
+    are checked here; the callers check its device afterwards."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not dense and t.dim() == 4 and t.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+
+
 def fa_strerror(code: int) -> str:
     return load_library().fa_strerror(int(code)).decode()
 
@@ -210,17 +239,26 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16,
                                                              torch.float32):
         raise TypeError("q, k, v must all be bfloat16, all float16 or all float32")
+    B, H, N, d = q.shape
+    if out is not None:
+        _check_out(out, "out", q.shape, q.dtype, dense=q.dtype == torch.float32)
+    if lse is not None:
+        _check_out(lse, "lse", (B, H, N), torch.float32, dense=True)
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
-    B, H, N, d = q.shape
+    if not (k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one device")
+    for t, name in ((out, "out"), (lse, "lse")):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}, got {t.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _resolve_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     dense = all(t.is_contiguous() for t in (q, k, v, out))
     if q.dtype == torch.float32:
         if not dense:
@@ -256,21 +294,26 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape")
     if not all(t.dtype == q.dtype for t in ts) or q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("q, k, v, o, dout must all be bfloat16 or all float16")
-    if lse.dtype != torch.float32:
-        raise TypeError("lse must be float32")
+    B, H, N, d = q.shape
+    _check_out(lse, "lse", (B, H, N), torch.float32, dense=True)
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be a (dq, dk, dv) triple")
+        for t, name in zip(out, ("dq", "dk", "dv")):
+            _check_out(t, name, q.shape, q.dtype)
     if not all(t.is_cuda for t in ts + (lse,)):
         raise ValueError("all tensors must be device tensors")
-    B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous [B, H, N] tensor")
+    for t in ts[1:] + (lse,) + (tuple(out) if out is not None else ()):
+        if t.device != q.device:
+            raise ValueError(f"every tensor must be on {q.device}, got {t.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = tuple(torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    stream = _resolve_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = tuple(torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     dq, dk, dv = out
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     tensors = ts + (dq, dk, dv)
     if q.dtype == torch.bfloat16 and all(t.is_contiguous() for t in tensors):
         rc = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
@@ -302,20 +345,25 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits
         raise ValueError("need q [B, H, Nq, d] and k, v [B, H, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("q, k, v must all be bfloat16 or all float16")
-    if not all(t.is_cuda for t in (q, k, v)):
-        raise ValueError("q, k, v must be device tensors")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
+    if out is not None:
+        _check_out(out, "out", q.shape, q.dtype)
+    if not all(t.is_cuda for t in (q, k, v)):
+        raise ValueError("q, k, v must be device tensors")
+    for t in (k, v) + ((out,) if out is not None else ()):
+        if t.device != q.device:
+            raise ValueError(f"every tensor must be on {q.device}, got {t.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits)
     if need == 0:
         raise FAError(FA_ERR_SHAPE, fa_strerror(FA_ERR_SHAPE))
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = torch.empty(q.shape, dtype=q.dtype, device=q.device) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _resolve_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        o = torch.empty(q.shape, dtype=q.dtype, device=q.device) if out is None else out
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     tensors = (q, k, v, o)
     if q.dtype == torch.bfloat16 and all(t.is_contiguous() for t in tensors):
         rc = fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, ws, need,
@@ -349,11 +397,11 @@ def forward_kv_outer(q, k, v, causal: bool = False, scale: float | None = None, 
     need = fa_fwd_kv_outer_workspace_size(B, H, N, d)
     if need == 0:
         raise FAError(FA_ERR_SHAPE, fa_strerror(FA_ERR_SHAPE))
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _resolve_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     rc = fa_fwd_kv_outer(q, k, v, o, lse, B, H, N, d, scale, causal, ws, need, stream)
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))

@@ -19,6 +19,16 @@ bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) 
 // Head dims of every entry point: multiples of 16 from 16 to 128.
 bool head_dim_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 
+// Launch-size limit: at most 2^22 (batch*head, 128-row block) pairs, so that
+// no kernel of a call launches 2^31 or more work-items (the largest grid,
+// 512 threads per 256 rows, stays within 2^31) and every workgroup count fits
+// an int.  Decode adds the same bound on its B*H*Nq output rows (one
+// 256-thread merge workgroup each).
+constexpr uint64_t kMaxRowBlocks = 1ull << 22;
+bool grid_ok(int B, int H, int N) {
+    return (uint64_t)B * (uint64_t)H * (((uint64_t)N + 127) / 128) <= kMaxRowBlocks;
+}
+
 int validate(const void *q, const void *k, const void *v, const void *o, const void *lse,
              int B, int H, int N, int d, float scale, uint64_t elem_bytes) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
@@ -27,6 +37,7 @@ int validate(const void *q, const void *k, const void *v, const void *o, const v
     // B*H*N*d < 2^40, evaluated without overflow (N*d < 2^38, B*H < 2^62).
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
+    if (!grid_ok(B, H, N)) return FA_ERR_SHAPE;
     const uint64_t rows = bh * (uint64_t)N;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
     for (const void *p : {q, k, v, o, lse})
@@ -51,6 +62,7 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o, con
     if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
     if (bh > ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d)) return FA_ERR_SHAPE;
+    if (!grid_ok(B, H, N)) return FA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
     for (const void *p : {q, k, v, o, dout, lse, dq, dk, dv, delta})
         if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
@@ -75,6 +87,7 @@ bool decode_shape_ok(int B, int H, int Nq, int Nk, int d) {
         return false;
     if (!head_dim_ok(d)) return false;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    if (bh * (uint64_t)Nq > kMaxRowBlocks || !grid_ok(B, H, Nk)) return false;
     return bh <= ((1ull << 40) - 1) / ((uint64_t)Nk * (uint64_t)d);
 }
 
@@ -100,7 +113,7 @@ bool shape_ok(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || N > (1 << 30)) return false;
     if (!head_dim_ok(d)) return false;
     const uint64_t bh = (uint64_t)B * (uint64_t)H;
-    return bh <= ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d);
+    return grid_ok(B, H, N) && bh <= ((1ull << 40) - 1) / ((uint64_t)N * (uint64_t)d);
 }
 
 // Byte span of a strided [B, H, N, d] view of 2-byte elements: one past the
@@ -359,7 +372,7 @@ const char *fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: need B, H, N >= 1, N <= 2^30 and B*H*N*d < 2^40";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: need B, H, N >= 1, N <= 2^30, B*H*N*d < 2^40 and B*H*ceil(N/128) <= 2^22";
         case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension d not supported (need a multiple of 16 from 16 to 128)";
         case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";

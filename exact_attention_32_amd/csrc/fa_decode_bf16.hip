@@ -712,24 +712,6 @@ hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float 
 
 }  // namespace
 
-int decode_num_splits(int B, int H, int Nk, int requested) {
-    if (requested > 0) return min(requested, (Nk + kDecodeMinChunk - 1) / kDecodeMinChunk);
-    // About kDecodeTargetWaves single-wave workgroups in all, chunks of at
-    // least kDecodeMinChunk keys.
-    const long bh = (long)B * H;
-    long s = (kDecodeTargetWaves + bh - 1) / bh;
-    const long smax = (Nk + kDecodeMinChunk - 1) / kDecodeMinChunk;
-    if (s > smax) s = smax;
-    if (s < 1) s = 1;
-    return (int)s;
-}
-
-int decode_chunk(int Nk, int S) {
-    // a multiple of 64 keys (whole blocks of loads at both head dims)
-    const int c = (Nk + S - 1) / S;
-    return (c + 63) / 64 * 64;
-}
-
 hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                               int B, int H, int Nq, int Nk, int d, float scale, bool causal,
                               int S, float *o_part, float *lse_part, hipStream_t stream) {

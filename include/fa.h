@@ -33,8 +33,10 @@
  *            in fp32.  (The pages keep the row maximum m and sum l, first
  *            page, section 4, last steps of Algorithm 1; this library returns
  *            the single number m*scale + ln(l) instead.)
- * Shapes:    B, H, N >= 1; N <= 2^30; B*H*N*d < 2^40; the head dim d is
- *            a multiple of 16 from 16 to 128 for every entry point.
+ * Shapes:    B, H, N >= 1; N <= 2^30; B*H*N*d < 2^40; B*H*ceil(N/128)
+ *            <= 2^22 (a launch-size limit: no kernel then launches 2^31 or
+ *            more work-items; decode also needs B*H*Nq <= 2^22); the head dim
+ *            d is a multiple of 16 from 16 to 128 for every entry point.
  * scale:     finite and > 0 (usually 1/sqrt(d)).
  * causal:    0 = no mask, any other value = top-left causal mask.
  * Errors:    all argument checks run before anything is enqueued; a failed
@@ -57,7 +59,8 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = 1,     /* a required pointer is NULL                       */
-    FA_ERR_SHAPE = 2,    /* B, H or N < 1, N > 2^30, or B*H*N*d >= 2^40      */
+    FA_ERR_SHAPE = 2,    /* B, H or N < 1, N > 2^30, B*H*N*d >= 2^40, or     */
+                         /* B*H*ceil(N/128) > 2^22 (launch-size limit)       */
     FA_ERR_HEADDIM = 3,  /* d not supported by the entry point (see Shapes)  */
     FA_ERR_SCALE = 4,    /* scale is not finite, or not > 0                  */
     FA_ERR_ALIGN = 5,    /* a pointer is not 16-byte aligned                 */
@@ -155,7 +158,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
  *               bytes for the fp32 partials; its contents on return are
  *               unspecified; it must not overlap any other argument
  * Scores, statistics and sums are fp32.  Shapes: B, H >= 1, 1 <= Nq <= 16,
- * Nq <= Nk <= 2^30, d a multiple of 16 up to 128, B*H*Nk*d < 2^40.  Two
+ * Nq <= Nk <= 2^30, d a multiple of 16 up to 128, B*H*Nk*d < 2^40,
+ * B*H*ceil(Nk/128) <= 2^22 and B*H*Nq <= 2^22 (launch-size limits).  Two
  * kernels are enqueued on `stream`.  Errors as for fa_fwd, plus
  * FA_ERR_WORKSPACE.
  */

@@ -93,6 +93,28 @@ def test_validation_codes(fn, lib):
     assert _call(fn, o=Q + nbytes, B=0) == fa.FA_ERR_SHAPE
 
 
+def test_launch_size_limit(lib):
+    """B*H*ceil(N/128) <= 2^22: no kernel launches 2^31 or more work-items.
+    At the limit the shape passes (the call then fails on the scale, before
+    any launch); one (batch*head, 128-row block) pair more is FA_ERR_SHAPE."""
+    for fn in (fa.fa_fwd, fa.fa_fwd_f32):
+        assert _call(fn, B=1 << 12, H=1 << 10, N=1, d=16, scale=0.0) == fa.FA_ERR_SCALE
+        assert _call(fn, B=1 << 12, H=(1 << 10) + 1, N=1, d=16) == fa.FA_ERR_SHAPE
+        assert _call(fn, B=1 << 11, H=1 << 10, N=256, d=16, scale=0.0) == fa.FA_ERR_SCALE
+        assert _call(fn, B=1 << 11, H=1 << 10, N=257, d=16) == fa.FA_ERR_SHAPE
+    assert _bwd(B=1 << 12, H=1 << 10, N=128, d=16, scale=0.0) == fa.FA_ERR_SCALE
+    assert _bwd(B=1 << 12, H=1 << 10, N=129, d=16) == fa.FA_ERR_SHAPE
+    ws = fa.fa_decode_workspace_size
+    assert ws(1 << 18, 1, 16, 16, 16, 1) > 0                     # B*H*Nq = 2^22
+    assert ws((1 << 18) + 1, 1, 16, 16, 16, 1) == 0              # one merge row too many
+    assert ws(1 << 22, 1, 1, 128, 16, 1) > 0                     # B*H*ceil(Nk/128) = 2^22
+    assert ws(1 << 22, 1, 1, 129, 16, 1) == 0
+    assert fa.fa_fwd_kv_outer_workspace_size(1 << 12, 1 << 10, 129, 16) == 0
+    rc = fa.fa_decode(Q, K, V, O, L, (1 << 18) + 1, 1, 16, 16, 16, 0.25, 0, 1, BASE + 7 * GAP,
+                      1 << 40, None)
+    assert rc == fa.FA_ERR_SHAPE
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from exact_attention_32_amd import _lib
 

@@ -99,13 +99,17 @@ def test_bwd_small_shapes(B, H, N, d, dist, causal, oracle_lib):
 
 
 def _sample_keys(w, rng, count):
-    """Keys whose dK/dV the oracle can afford at full size: any key without
-    the mask (all rows see it anyway), the last 96 keys with it (only the
-    last rows see them), plus the first and last key."""
+    """Keys whose dK/dV the oracle checks element by element at full size:
+    without the mask, any keys (every row sees every key); with it, random
+    keys among the last 96 (seen by the last rows only) and the early keys
+    0, 1, 63, 64 and N/2, which every later query sees: their dK/dV sum over
+    the longest accumulations (up to N queries) and cross the first key-tile
+    boundary."""
     if not w.causal:
         return np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, count)]))
     lo = max(0, w.N - 96)
-    return np.unique(np.concatenate([[w.N - 1, lo], rng.integers(lo, w.N, count)]))
+    early = [j for j in (0, 1, 63, 64, w.N // 2) if j < w.N]
+    return np.unique(np.concatenate([early, [w.N - 1, lo], rng.integers(lo, w.N, count)]))
 
 
 @pytest.mark.parametrize("name", ["w2_bf16_b4h16_n2048_d64", "w3_bf16_b2h32_n8192_d128_causal",

@@ -75,24 +75,72 @@ def test_workload_full_tensor(name, oracle_lib):
     full_case(inputs.WORKLOADS[name], oracle_lib)
 
 
-# --- the two largest workloads: sampled rows, computed one by one ----------
-@pytest.mark.parametrize("name", ["w3_bf16_b2h32_n8192_d128_causal",
-                                  "w4_bf16_b1h16_n16384_d64_causal_big_logits"])
-def test_workload_sampled_rows(name, oracle_lib):
-    w = inputs.WORKLOADS[name]
-    _say(f"case {w.name} (sampled rows)")
-    q, k, v = inputs.make_qkv(w)
-    o, lse = run_gpu(q, k, v, w.causal, w.scale)
-    rows = inputs.sample_rows(w, 384)
-    # every causal row 0 sees exactly key 0: O[0] must equal V[0] bit for bit
-    o0 = o[:, :, 0]
-    v0 = v[:, :, 0].float().double().numpy()
-    assert np.array_equal(o0, v0), "causal row 0 differs from V[0]"
-    o_ref, lse_ref = oracle_lib.attention_rows(q, k, v, w.scale, w.causal, rows)
-    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
-    got_lse = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
-    check(got, got_lse, o_ref, lse_ref, w.dtype, w.name + " sampled")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+# --- the two largest workloads, over the whole tensor ------------------------
+# The GPU runs each workload once (cached for the module); the oracle then
+# evaluates every head, a group of heads per test so that each test reports
+# within a few seconds, and the gates apply to the whole tensor: max-abs and
+# LSE over every element, relative L2 over the accumulated sums of squares.
+BIG = ["w3_bf16_b2h32_n8192_d128_causal", "w4_bf16_b1h16_n16384_d64_causal_big_logits"]
+BIG_GROUPS = 8
+_big_state = {}
+
+
+def _big(name):
+    if name not in _big_state:
+        w = inputs.WORKLOADS[name]
+        _say(f"case {w.name}: GPU run (whole tensor)")
+        q, k, v = inputs.make_qkv(w)
+        o, lse = run_gpu(q, k, v, w.causal, w.scale)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"{name}: non-finite output"
+        # every causal row 0 sees exactly key 0: O[0] must equal V[0] bit for bit
+        if w.causal:
+            assert np.array_equal(o[:, :, 0], v[:, :, 0].float().double().numpy()), \
+                f"{name}: causal row 0 differs from V[0]"
+        _big_state[name] = dict(w=w, q=q, k=k, v=v, o=o, lse=lse, done=set(), err2=0.0, ref2=0.0,
+                                max_abs=0.0, lse_err=0.0)
+    return _big_state[name]
+
+
+def _big_group(name, group, oracle_lib):
+    st = _big(name)
+    if group in st["done"]:
+        return st
+    w = st["w"]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    mine = heads[group::BIG_GROUPS]
+    for b, h in mine:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, lse_ref = oracle_lib.attention(st["q"][sl], st["k"][sl], st["v"][sl], w.scale,
+                                              w.causal)
+        got, got_lse = st["o"][sl], st["lse"][sl]
+        err = got - o_ref
+        st["err2"] += float(np.sum(err * err))
+        st["ref2"] += float(np.sum(o_ref * o_ref))
+        st["max_abs"] = max(st["max_abs"], float(np.abs(err).max()))
+        st["lse_err"] = max(st["lse_err"], float(np.abs(got_lse - lse_ref).max()))
+    st["done"].add(group)
+    _say(f"  {name} heads {[b * w.H + h for b, h in mine]}: running max_abs={st['max_abs']:.3e} "
+         f"lse={st['lse_err']:.3e}")
+    assert st["max_abs"] <= TOL_BF16_ABS, f"{name}: max abs {st['max_abs']}"
+    assert st["lse_err"] <= TOL_LSE, f"{name}: LSE {st['lse_err']}"
+    return st
+
+
+@pytest.mark.parametrize("name,group", [(n, g) for n in BIG for g in range(BIG_GROUPS)])
+def test_big_workload_heads(name, group, oracle_lib):
+    _big_group(name, group, oracle_lib)
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_big_workload_whole_tensor(name, oracle_lib):
+    for g in range(BIG_GROUPS):           # any group not run yet (e.g. under -k)
+        _big_group(name, g, oracle_lib)
+    st = _big_state[name]
+    rel = (st["err2"] / st["ref2"]) ** 0.5
+    _say(f"  {name} whole tensor: max_abs={st['max_abs']:.3e} rel_l2={rel:.3e} "
+         f"lse={st['lse_err']:.3e}")
+    assert st["max_abs"] <= TOL_BF16_ABS and rel <= TOL_BF16_REL and st["lse_err"] <= TOL_LSE
+    del _big_state[name]                  # free the host copies
 
 
 # --- reduced shapes: several tiles, ragged tails, both head dims -------------
