@@ -12,6 +12,9 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
+# The checking build (FA_SAFE_SYNC=1: every LDS copy completed at a barrier
+# before use); only the tests load it.
+SAFE_SYNC_LIB_PATH = os.path.join(HERE, "libfa_safesync.so")
 
 FA_OK = 0
 FA_ERR_NULL = 1
@@ -45,6 +48,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A fresh handle on a build of the library at ``path`` (e.g. the checking
+    build libfa_safesync.so) with the C ABI's argument types declared."""
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is not built; run `python -m exact_attention_32_amd.build_lib` "
@@ -75,7 +85,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_kv_outer_workspace_size.argtypes = [i] * 4
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [i]
-    _lib = lib
     return lib
 
 

@@ -187,6 +187,10 @@ bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restr
             load_tile<D, DH, STRIDED>(Kh, N, c0 + kInner, nk, ksrc, wave, kn);
             load_tile<D, DH, STRIDED>(Vh, N, c0 + kInner, nv, vsrc, wave, vn);
         }
+        if constexpr (kSafeSync) {  // checking build: the copies land before any compute
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
         if (active) {
             // S^T = K Q^T and dP^T = V dO^T (keys x queries).
@@ -351,6 +355,10 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
                     LDS3 char *nq, LDS3 char *no, LDS3 float *nst) {
         const int c0 = t * kInner;
         if (t + 1 < n_tiles) load_all(c0 + kInner, nq, no, nst);
+        if constexpr (kSafeSync) {  // checking build: the copies land before any compute
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
         // A wave whose keys all follow this query tile has nothing to add.
         const bool active = !CAUSAL || c0 + kInner - 1 >= wk0;
         if (active) {

@@ -428,6 +428,10 @@ decode_mfma_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     float m_run = -INFINITY, mc_run = -INFINITY, l_run = 0.f;
+    // Sum of the rounded probabilities that multiply V (the partial output is
+    // normalised by it; the partial LSE uses the fp32 sum l).
+    float lr_run = 0.f;
+    const X8 sel = rowsum_selector<E>(lane);
 
     // Probabilities of the tile's 32 keys against base mcx (scaled log2
     // units) as P^T operands (keys 0-15, 16-31), and their half-wave sum.
@@ -486,6 +490,7 @@ decode_mfma_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__
             mc_run = m_use * scale_log2;
             m_run = m_use;
             l_run *= alpha;
+            lr_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -498,9 +503,14 @@ decode_mfma_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 acc[db] = TileOps<E>::mfma(tr_read<D, X8>(vt, trd, tt, db), pp[tt], acc[db]);
+        f32x4 lt = {0.f, 0.f, 0.f, 0.f};
+        lt = TileOps<E>::mfma16(sel, pp[0], lt);
+        lt = TileOps<E>::mfma16(sel, pp[1], lt);
+        lr_run += lt[0];
         // every read of these buffers has completed before they are refilled
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         copy_tile(t + 3, kt, vt);
+        if constexpr (kSafeSync) __builtin_amdgcn_s_waitcnt(0);  // checking build
     };
 
     LDS3 char *const kb0 = (LDS3 char *)lk0;
@@ -531,7 +541,7 @@ decode_mfma_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__
     }
     if (j < Nq) {
         const size_t prow = ((size_t)bh * S + s) * Nq + j;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = lr_run > 0.f ? 1.f / lr_run : 0.f;
         float *dst = o_part + prow * DH;
 #pragma unroll
         for (int db = 0; db < DB; ++db)

@@ -70,6 +70,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -100,6 +101,9 @@ struct Elem<__bf16> {
     static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
 };
 template <>
 struct Elem<_Float16> {
@@ -108,7 +112,31 @@ struct Elem<_Float16> {
     static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
 };
+
+// Row sums of the rounded probabilities, on the matrix core.  The output is
+// normalised by the sum of exactly the (bf16 / fp16) probabilities that
+// multiplied V, so numerator and denominator carry the same rounding; the LSE
+// keeps the sum of the unrounded fp32 probabilities.  A P^T operand of
+// O^T += V^T P^T (lane l: query l % 32, keys 8(l / 32) .. +7 of a 16-key step)
+// is taken as the B operand of a 16 x 16 x 32 MFMA, which reads lane l as
+// column l % 16, reduction index 8(l / 16) .. +7.  Columns thus hold query n
+// in lane groups 0 and 2 and query n + 16 in groups 1 and 3; the 0/1 selector
+// A (row m takes reduction group k / 8 when (m / 4) and (k / 8) have the same
+// parity) makes output (m, n) the 16-key sum of query n (m / 4 even) or n + 16
+// (m / 4 odd), and the output layout (lane l: column l % 16, rows
+// 4(l / 16) .. +3) then gives every lane four copies of its own query's sum.
+template <typename E>
+__device__ __forceinline__ typename Elem<E>::x8 rowsum_selector(int lane) {
+    typename Elem<E>::x8 a;
+    const float one = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (E)one;
+    return a;
+}
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -390,6 +418,8 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     float m_run = -INFINITY;  // exponent base of row qrow (raw score units)
     float mc_run = -INFINITY; // the base in scaled log2 units (m_run * scale_log2)
     float l_run = 0.f;        // this half-wave's share of the running sum
+    float lr_run = 0.f;       // running sum of the rounded probabilities (whole row)
+    const X8 sel = rowsum_selector<E>(lane);
 
     LDS3 char *const k0 = (LDS3 char *)lds_k0;
     LDS3 char *const k1 = (LDS3 char *)lds_k1;
@@ -407,9 +437,20 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
                                                  wave, kn, vn);
         };
 
+        // Checking build: the next tile is copied and visible before this
+        // tile's compute starts (its buffers were released at the barrier
+        // that ended the previous tile).
+        if constexpr (kSafeSync) {
+            if (prefetch) {
+#pragma unroll
+                for (int i = 0; i < 2 * kLoads; ++i) load(i);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
         // A wave whose rows all precede this tile has nothing to add.
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
-        if (!active && prefetch) {
+        if (!active && prefetch && !kSafeSync) {
 #pragma unroll
             for (int i = 0; i < 2 * kLoads; ++i) load(i);
         }
@@ -442,7 +483,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
 #pragma unroll
                 for (int kb = 0; kb < kBc / 32; ++kb)
                     s[kb] = Elem<E>::mfma(kf[ks][kb], qop[ks], s[kb]);
-                if (prefetch) {
+                if (prefetch && !kSafeSync) {
 #pragma unroll
                     for (int i = ks * kTileLoads / KS; i < (ks + 1) * kTileLoads / KS; ++i) load(i);
                 }
@@ -531,6 +572,7 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                lr_run *= alpha;
                 exps(mc_run);
             }
             l_run += rs;
@@ -541,6 +583,10 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
                     acc[db] = Elem<E>::mfma(vf[T][db], pop[T], acc[db]);
+            f32x4 lt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int T = 0; T < kBc / 16; ++T) lt = Elem<E>::mfma16(sel, pop[T], lt);
+            lr_run += lt[0];
         }
 
         // The next tile's loads must have landed before anyone reads them, and
@@ -559,14 +605,15 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
         if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
     }
 
-    // Epilogue: O = acc / l, rounded to bf16; LSE = m*scale + ln(l).
+    // Epilogue: O = acc / (sum of the rounded probabilities), rounded to the
+    // element type; LSE = m*scale + ln(l) with the fp32 sum l.
     float l_tot;
     {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                          __float_as_uint(l_run), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / lr_run;
     if (qrow < N) {
         E *orow = O + ooff + (size_t)qrow * on;
 #pragma unroll
@@ -650,8 +697,8 @@ __device__ __forceinline__ void tile_load(const E *base, int rows, int rs, LDS3 
 template <typename E, int D, bool CAUSAL, bool STRIDED, int W>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
-                E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, float scale,
-                float scale_log2, FwdStrides st) {
+                E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int n_bh, int mode,
+                float scale, float scale_log2, FwdStrides st) {
     typedef typename Elem<E>::x8 X8;
     typedef typename Elem<E>::x4 X4;
     static_assert(D == 64 || D == 128, "head dim");
@@ -678,46 +725,15 @@ fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
     const int g = lane >> 5;
     const int j = lane & 31;
 
-    int bh, qt;
-    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, 32 * (8 / W), bh, qt);  // 8 / W per CU
-    const int r0 = qt * kRows;
-    size_t qoff, koff, voff, ooff;
-    int qn, kn, vn, on;
+    int qn, kn, vn, on;  // row strides (elements)
     if constexpr (STRIDED) {
-        const int b = bh / st.H, h = bh - b * st.H;
-        qoff = (size_t)(b * st.qb + h * st.qh);
-        koff = (size_t)(b * st.kb + h * st.kh);
-        voff = (size_t)(b * st.vb + h * st.vh);
-        ooff = (size_t)(b * st.ob + h * st.oh);
         qn = st.qn;
         kn = st.kn;
         vn = st.vn;
         on = st.on;
     } else {
-        qoff = koff = voff = ooff = (size_t)bh * (size_t)N * D;
         qn = kn = vn = on = D;
     }
-    const E *Qh = Q + qoff;
-    const E *Kh = K + koff;
-    const E *Vh = V + voff;
-    const int wrow0 = r0 + wave * kRowsPerWave;
-    const int qrow = wrow0 + j;
-
-    X8 qop[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
-        qop[ks] = __builtin_bit_cast(X8, x);
-    }
-
-    const int kv_end = CAUSAL ? min(N, r0 + kRows) : N;
-    const int n_tiles = (kv_end + kBc - 1) / kBc;
-    // Row qrow sees keys 0 .. vis (the element mask below); the wave's rows
-    // see keys up to vis_max at most.
-    const int vis = CAUSAL ? min(qrow, N - 1) : N - 1;
-    const int vis_max = CAUSAL ? wrow0 + kRowsPerWave - 1 : N - 1;
-
     // Gather offsets of the lane's first tile load (see tile_load).
     uint32_t k_src, v_src;
     {
@@ -742,266 +758,396 @@ fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
         v_rd[db] = (uint32_t)(row * D * 2 + ((c ^ v_swz<D>(row)) << 4) + ((col & 4) << 1));
     }
 
-    f32x16 acc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m_run = -INFINITY;   // exponent base of row qrow (raw score units)
-    float mc_run = -INFINITY;  // the base times scale * log2(e)
-    float l_run = 0.f;         // this half-wave's share of the running sum
-
+    const X8 sel = rowsum_selector<E>(lane);
     LDS3 char *const kb[kPipeBufs] = {(LDS3 char *)lds_k0, (LDS3 char *)lds_k1,
                                       (LDS3 char *)lds_k2};
     LDS3 char *const vb[kPipeBufs] = {(LDS3 char *)lds_v0, (LDS3 char *)lds_v1,
                                       (LDS3 char *)lds_v2};
 
-    // LDS reads of MFMA pair i of a step: the V^T fragment (i / DB, i % DB)
-    // of half `hv` of tile buffer vt (two transpose reads) and the K
-    // fragment of k-step i of half `hk` of tile buffer kt.
-    auto read_pair = [&](int i, const LDS3 char *kt, int hk, const LDS3 char *vt, int hv, X8 &vfr,
-                         X8 &kfr) __attribute__((always_inline)) {
-        const LDS3 char *base = vt + v_rd[i % DB] + (2 * hv + i / DB) * 16 * D * 2;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
-        vfr = __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        kfr = *reinterpret_cast<const LDS3 X8 *>(kt + k_rd[i] + hk * 32 * D * 2);
-    };
-
-    // Element r of a half tile's S^T block is key 32h + 8(r/4) + 4g + r%4 of
-    // query qrow; its P^T operands p[0], p[1] cover keys 32h .. +15 and
-    // 32h+16 .. +31 (k-steps of O^T += V^T P^T).
-    //
-    // Probabilities of one half tile against exponent base mcx (scaled log2
-    // units) as P^T operands, and their (half-wave) sum.
-    auto exps = [&](const f32x16 &s, float mcx, X8 (&p)[2]) __attribute__((always_inline)) {
-        f32x8 lo, hi;
-        float ra = 0.f, rb = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -mcx));
-            hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 8], scale_log2, -mcx));
-            ra += lo[r];
-            rb += hi[r];
+    // Static schedule (no atomics, no dispatcher involvement after the
+    // launch): the grid is sized to the workgroup slots of the device and each
+    // workgroup walks its own list of query tiles.  Workgroup w runs on XCD
+    // w mod 8 (workgroups are dealt round-robin over the XCDs).
+    //  * mode 2 (the grid and the heads both divide by 8): XCD x owns heads
+    //    x, x+8, ...; its L = G/8 workgroups take its (head, tile) items in
+    //    rounds of L, head-major with the longest causal tiles first, in snake
+    //    order (round r: workgroup lw takes item rL + lw, or rL + L-1-lw when r
+    //    is odd).  Causal costs fall linearly along a head, so two
+    //    consecutive rounds give every workgroup the same work, and an XCD
+    //    works on about one head at a time, whose K/V its L2 then serves.
+    //  * mode 1 (causal, enough heads to fill the grid): units are the tile
+    //    pairs (nqt-1-i, i) of a head, equal in cost, taken round-robin.
+    //  * mode 0: single tiles round-robin, longest causal tiles first over
+    //    all heads.
+    //  * mode 3: one tile per workgroup, the grid covering every tile, mapped
+    //    by map_block (the dispatcher then balances the workgroups).
+    const int npairs = mode == 1 ? (nqt + 1) / 2 : nqt;
+    const int n_units = n_bh * npairs;
+    const int G = gridDim.x;
+    const int L = G >> 3;
+    const int x = blockIdx.x & 7, lw = blockIdx.x >> 3;
+    const int n_local = (n_bh >> 3) * nqt;
+    const int slot = ((G & 7) == 0) ? x * L + lw : (int)blockIdx.x;
+    for (int it = 0;; ++it) {
+        int bh, qt;
+        if (mode == 3) {
+            if (it > 0) break;
+            map_block(blockIdx.x, G, nqt, CAUSAL, 32 * (8 / W), bh, qt);
+        } else if (mode == 2) {
+            if (it * L >= n_local) break;
+            const int pos = it * L + ((it & 1) ? (L - 1 - lw) : lw);
+            if (pos >= n_local) continue;
+            const int lh = pos / nqt, pq = pos - lh * nqt;
+            bh = lh * 8 + x;
+            qt = CAUSAL ? nqt - 1 - pq : pq;
+        } else if (mode == 1) {
+            const int unit = slot + (it >> 1) * G;
+            if (unit >= n_units) break;
+            bh = unit / npairs;
+            const int pi = unit - bh * npairs;
+            if (it & 1) {
+                if (nqt - 1 - pi == pi) continue;  // the middle tile of an odd count
+                qt = pi;
+            } else {
+                qt = nqt - 1 - pi;
+            }
+        } else {
+            const int unit = slot + it * G;
+            if (unit >= n_units) break;
+            if (CAUSAL) {
+                const int rank = unit / n_bh;
+                bh = unit - rank * n_bh;
+                qt = nqt - 1 - rank;
+            } else {
+                bh = unit / nqt;
+                qt = unit - bh * nqt;
+            }
         }
-        p[0] = __builtin_convertvector(lo, X8);
-        p[1] = __builtin_convertvector(hi, X8);
-        return ra + rb;
-    };
-    // Slow path of the lazy base: the base moves to the row maximum, the
-    // accumulator and the sum are rescaled, the probabilities recomputed.
-    auto rebase = [&](const f32x16 &s, X8 (&p)[2]) __attribute__((always_inline)) {
-        float mt = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
         {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                             false, false);
-            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha =
-            (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
-        mc_run = m_use * scale_log2;
-        m_run = m_use;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        return exps(s, mc_run, p);
-    };
+            // Every wave is done with the previous tile's LDS buffers (and
+            // its copies have landed) before this tile's prologue refills them.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const int r0 = qt * kRows;
+            size_t qoff, koff, voff, ooff;
+            if constexpr (STRIDED) {
+                const int b = bh / st.H, h = bh - b * st.H;
+                qoff = (size_t)(b * st.qb + h * st.qh);
+                koff = (size_t)(b * st.kb + h * st.kh);
+                voff = (size_t)(b * st.vb + h * st.vh);
+                ooff = (size_t)(b * st.ob + h * st.oh);
+            } else {
+                qoff = koff = voff = ooff = (size_t)bh * (size_t)N * D;
+            }
+            const E *Qh = Q + qoff;
+            const E *Kh = K + koff;
+            const E *Vh = V + voff;
+            const int wrow0 = r0 + wave * kRowsPerWave;
+            const int qrow = wrow0 + j;
 
-    // Step h.  (kt, hk): LDS tile buffer and half holding the K rows of half
-    // tile h+1; (vt, hv): those holding the V rows of half tile h-1;
-    // (ktn, hkn), (vtn, hvn): the same for step h+1, whose first two MFMA
-    // pairs' operands this step reads at its end.  vf0/kf0: this step's
-    // first two pairs' operands (in), the next step's (out).  sc: scores of
-    // half tile h (in), sn: scores of half tile h+1 (out); pp: P^T of half
-    // tile h-1 (in), pc: P^T of half tile h (out).  With LOADS, the step
-    // also issues the copies of K(t+3) into kload and V(t+2) into vload
-    // (t = the tile of half tile h).  Every buffer a step reads has been
-    // filled (possibly with zeros past kv_end), so steps outside the wave's
-    // visible range compute finite, discarded scores and add zero
-    // probabilities.
-    auto step = [&](int h, auto loads_tag, const LDS3 char *kt, int hk, const LDS3 char *vt, int hv,
-                    const LDS3 char *ktn, int hkn, const LDS3 char *vtn, int hvn,
-                    LDS3 char *kload, LDS3 char *vload, X8 (&vf0)[2], X8 (&kf0)[2], f32x16 &sc,
-                    f32x16 &sn, X8 (&pp)[2], X8 (&pc)[2]) __attribute__((always_inline)) {
-        constexpr bool LOADS = decltype(loads_tag)::value;
-        // Element mask of half tile h: visible iff 8(r/4) + r%4 <= lim.
-        const int lim = vis - 32 * h - 4 * g;
-        if (32 * h + 31 > (CAUSAL ? wrow0 : N - 1)) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (8 * (r >> 2) + (r & 3) > lim) sc[r] = -INFINITY;
-        }
-        // MFMA pair i: P V^T with V^T fragment (i / DB, i % DB), then K Q^T
-        // k-step i.  LDS reads in the order of use: pairs 2 .. KS-1 of this
-        // step, then pairs 0, 1 of the next.
-        X8 vf[KS], kf[KS];
-        vf[0] = vf0[0];
-        kf[0] = kf0[0];
-        vf[1] = vf0[1];
-        kf[1] = kf0[1];
-#pragma unroll
-        for (int i = 2; i < KS; ++i) read_pair(i, kt, hk, vt, hv, vf[i], kf[i]);
-        read_pair(0, ktn, hkn, vtn, hvn, vf0[0], kf0[0]);
-        read_pair(1, ktn, hkn, vtn, hvn, vf0[1], kf0[1]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sn[r] = 0.f;
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            acc[i % DB] = Elem<E>::mfma(vf[i], pp[i / DB], acc[i % DB]);
-            sn = Elem<E>::mfma(kf[i], qop[i], sn);
-        }
-        float rs = exps(sc, mc_run, pc);
-        if constexpr (LOADS) {
-            const int t = h >> 1;
-            const E *kbase = Kh + (size_t)(t + 3) * kBc * kn;
-            const E *vbase = Vh + (size_t)(t + 2) * kBc * vn;
-            const int krows = min(kBc, kv_end - (t + 3) * kBc);
-            const int vrows = min(kBc, kv_end - (t + 2) * kBc);
-#pragma unroll
+            X8 qop[KS];
+        #pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
+                qop[ks] = __builtin_bit_cast(X8, x);
+            }
+
+            const int kv_end = CAUSAL ? min(N, r0 + kRows) : N;
+            const int n_tiles = (kv_end + kBc - 1) / kBc;
+            // Row qrow sees keys 0 .. vis (the element mask below); the wave's rows
+            // see keys up to vis_max at most.
+            const int vis = CAUSAL ? min(qrow, N - 1) : N - 1;
+            const int vis_max = CAUSAL ? wrow0 + kRowsPerWave - 1 : N - 1;
+
+            f32x16 acc[DB];
+        #pragma unroll
+            for (int db = 0; db < DB; ++db)
+        #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+            float m_run = -INFINITY;   // exponent base of row qrow (raw score units)
+            float mc_run = -INFINITY;  // the base times scale * log2(e)
+            float l_run = 0.f;         // this half-wave's share of the running sum
+            float lr_run = 0.f;        // running sum of the rounded probabilities (whole row)
+
+
+            // LDS reads of MFMA pair i of a step: the V^T fragment (i / DB, i % DB)
+            // of half `hv` of tile buffer vt (two transpose reads) and the K
+            // fragment of k-step i of half `hk` of tile buffer kt.
+            auto read_pair = [&](int i, const LDS3 char *kt, int hk, const LDS3 char *vt, int hv, X8 &vfr,
+                                 X8 &kfr) __attribute__((always_inline)) {
+                const LDS3 char *base = vt + v_rd[i % DB] + (2 * hv + i / DB) * 16 * D * 2;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
+                vfr = __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                kfr = *reinterpret_cast<const LDS3 X8 *>(kt + k_rd[i] + hk * 32 * D * 2);
+            };
+
+            // Element r of a half tile's S^T block is key 32h + 8(r/4) + 4g + r%4 of
+            // query qrow; its P^T operands p[0], p[1] cover keys 32h .. +15 and
+            // 32h+16 .. +31 (k-steps of O^T += V^T P^T).
+            //
+            // Probabilities of one half tile against exponent base mcx (scaled log2
+            // units) as P^T operands, and their (half-wave) sum.
+            auto exps = [&](const f32x16 &s, float mcx, X8 (&p)[2]) __attribute__((always_inline)) {
+                f32x8 lo, hi;
+                float ra = 0.f, rb = 0.f;
+        #pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -mcx));
+                    hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 8], scale_log2, -mcx));
+                    ra += lo[r];
+                    rb += hi[r];
+                }
+                p[0] = __builtin_convertvector(lo, X8);
+                p[1] = __builtin_convertvector(hi, X8);
+                return ra + rb;
+            };
+            // Slow path of the lazy base: the base moves to the row maximum, the
+            // accumulator and the sum are rescaled, the probabilities recomputed.
+            auto rebase = [&](const f32x16 &s, X8 (&p)[2]) __attribute__((always_inline)) {
+                float mt = s[0];
+        #pragma unroll
+                for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+                {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                                     false, false);
+                    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                }
+                const float m_new = fmaxf(m_run, mt);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha =
+                    (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+                mc_run = m_use * scale_log2;
+                m_run = m_use;
+                l_run *= alpha;
+        #pragma unroll
+                for (int db = 0; db < DB; ++db)
+        #pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                lr_run *= alpha;
+                return exps(s, mc_run, p);
+            };
+
+            // Step h.  (kt, hk): LDS tile buffer and half holding the K rows of half
+            // tile h+1; (vt, hv): those holding the V rows of half tile h-1;
+            // (ktn, hkn), (vtn, hvn): the same for step h+1, whose first two MFMA
+            // pairs' operands this step reads at its end.  vf0/kf0: this step's
+            // first two pairs' operands (in), the next step's (out).  sc: scores of
+            // half tile h (in), sn: scores of half tile h+1 (out); pp: P^T of half
+            // tile h-1 (in), pc: P^T of half tile h (out).  With LOADS, the step
+            // also issues the copies of K(t+3) into kload and V(t+2) into vload
+            // (t = the tile of half tile h).  Every buffer a step reads has been
+            // filled (possibly with zeros past kv_end), so steps outside the wave's
+            // visible range compute finite, discarded scores and add zero
+            // probabilities.
+            auto step = [&](int h, auto loads_tag, const LDS3 char *kt, int hk, const LDS3 char *vt, int hv,
+                            const LDS3 char *ktn, int hkn, const LDS3 char *vtn, int hvn,
+                            LDS3 char *kload, LDS3 char *vload, X8 (&vf0)[2], X8 (&kf0)[2], f32x16 &sc,
+                            f32x16 &sn, X8 (&pp)[2], X8 (&pc)[2]) __attribute__((always_inline)) {
+                constexpr bool LOADS = decltype(loads_tag)::value;
+                // Element mask of half tile h: visible iff 8(r/4) + r%4 <= lim.
+                const int lim = vis - 32 * h - 4 * g;
+                if (32 * h + 31 > (CAUSAL ? wrow0 : N - 1)) {
+        #pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > lim) sc[r] = -INFINITY;
+                }
+                // MFMA pair i: P V^T with V^T fragment (i / DB, i % DB), then K Q^T
+                // k-step i.  LDS reads in the order of use: pairs 2 .. KS-1 of this
+                // step, then pairs 0, 1 of the next.
+                X8 vf[KS], kf[KS];
+                vf[0] = vf0[0];
+                kf[0] = kf0[0];
+                vf[1] = vf0[1];
+                kf[1] = kf0[1];
+        #pragma unroll
+                for (int i = 2; i < KS; ++i) read_pair(i, kt, hk, vt, hv, vf[i], kf[i]);
+                read_pair(0, ktn, hkn, vtn, hvn, vf0[0], kf0[0]);
+                read_pair(1, ktn, hkn, vtn, hvn, vf0[1], kf0[1]);
+        #pragma unroll
+                for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+                // Row sums of P^T of half tile h-1 (the operands of this step's
+                // P V^T), added to the running sum at the end of the step.
+                f32x4 lt = {0.f, 0.f, 0.f, 0.f};
+                lt = Elem<E>::mfma16(sel, pp[0], lt);
+                lt = Elem<E>::mfma16(sel, pp[1], lt);
+        #pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    acc[i % DB] = Elem<E>::mfma(vf[i], pp[i / DB], acc[i % DB]);
+                    sn = Elem<E>::mfma(kf[i], qop[i], sn);
+                }
+                float rs = exps(sc, mc_run, pc);
+                if constexpr (LOADS) {
+                    const int t = h >> 1;
+                    const E *kbase = Kh + (size_t)(t + 3) * kBc * kn;
+                    const E *vbase = Vh + (size_t)(t + 2) * kBc * vn;
+                    const int krows = min(kBc, kv_end - (t + 3) * kBc);
+                    const int vrows = min(kBc, kv_end - (t + 2) * kBc);
+        #pragma unroll
+                    for (int u = 0; u < kLoads; ++u) {
+                        tile_load<D, W, STRIDED>(kbase, krows, kn, kload, k_src, u, wave);
+                        tile_load<D, W, STRIDED>(vbase, vrows, vn, vload, v_src, u, wave);
+                    }
+                }
+                // Per pair: the three LDS reads of the pair two ahead (of the next
+                // step for the last two pairs), then each MFMA followed by its share
+                // of the softmax; the tile copies spread evenly.
+                constexpr int kValu = (56 + 2 * KS - 1) / (2 * KS);  // softmax VALU per MFMA
+                constexpr int kCopyEvery = KS / (2 * kLoads);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the two row-sum MFMAs
+        #pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+                    if (LOADS && i % kCopyEvery == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                lr_run += lt[0];  // before a rebase, which rescales it with acc
+                if (__ballot(!(rs <= kSumMax<E>))) rs = rebase(sc, pc);
+                l_run += rs;
+            };
+
+            f32x16 sA, sB;
+            X8 pA[2], pB[2] = {X8{}, X8{}};
+            X8 vf0[2], kf0[2];
+            const std::integral_constant<bool, true> with_loads;
+            const std::integral_constant<bool, false> no_loads;
+
+            // Prologue: K(0), K(1), K(2), V(0), V(1) into LDS (tile step t copies
+            // K(t+3) and V(t+2)); scores of half tile 0; step 0 (whose P V^T adds
+            // zeros).
+        #pragma unroll
             for (int u = 0; u < kLoads; ++u) {
-                tile_load<D, W, STRIDED>(kbase, krows, kn, kload, k_src, u, wave);
-                tile_load<D, W, STRIDED>(vbase, vrows, vn, vload, v_src, u, wave);
+        #pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    tile_load<D, W, STRIDED>(Kh + (size_t)i * kBc * kn, min(kBc, kv_end - i * kBc), kn, kb[i],
+                                             k_src, u, wave);
+        #pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    tile_load<D, W, STRIDED>(Vh + (size_t)i * kBc * vn, min(kBc, kv_end - i * kBc), vn, vb[i],
+                                             v_src, u, wave);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            {
+                X8 kf[KS];
+        #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const LDS3 X8 *>(kb[0] + k_rd[ks]);
+        #pragma unroll
+                for (int r = 0; r < 16; ++r) sA[r] = 0.f;
+        #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) sA = Elem<E>::mfma(kf[ks], qop[ks], sA);
+            }
+            read_pair(0, kb[0], 1, vb[0], 0, vf0[0], kf0[0]);
+            read_pair(1, kb[0], 1, vb[0], 0, vf0[1], kf0[1]);
+            // Step 0 reads K half tile 1 (tile 0, half 1); step 1 reads K tile 1
+            // half 0 and V tile 0 half 0.
+            step(0, no_loads, kb[0], 1, vb[0], 0, kb[1], 0, vb[0], 0, kb[0], vb[0], vf0, kf0, sA, sB, pB, pA);
+
+            // Tile step t (buffers b = t mod 3): step 2t+1 reads K(t+1) half 0 and
+            // V(t) half 0, step 2t+2 their halves 1, and step 2t+3 (read ahead) K(t+2)
+            // half 0 and V(t+1) half 0.  A wave whose last visible half tile hlast
+            // has had its P V^T (step hlast+1) leaves the loop; for the rest of the
+            // workgroup's tiles it only issues its share of the copies and meets the
+            // barriers.
+            const int hlast = (min(kv_end - 1, vis_max) >> 5);
+            // The copies of tile step t: K(t+3) into the buffer of K(t), V(t+2)
+            // into that of V(t-1).
+            auto copy_ahead = [&](int t, LDS3 char *kload, LDS3 char *vload)
+                                  __attribute__((always_inline)) {
+                const E *kbase = Kh + (size_t)(t + 3) * kBc * kn;
+                const E *vbase = Vh + (size_t)(t + 2) * kBc * vn;
+                const int krows = min(kBc, kv_end - (t + 3) * kBc);
+                const int vrows = min(kBc, kv_end - (t + 2) * kBc);
+#pragma unroll
+                for (int u = 0; u < kLoads; ++u) {
+                    tile_load<D, W, STRIDED>(kbase, krows, kn, kload, k_src, u, wave);
+                    tile_load<D, W, STRIDED>(vbase, vrows, vn, vload, v_src, u, wave);
+                }
+            };
+            auto tile_step = [&](int t, int b) __attribute__((always_inline)) {
+                const int b1 = (b + 1) % 3, b2 = (b + 2) % 3;
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if constexpr (kSafeSync) {
+                    // Checking build: the copies land and are visible before
+                    // the tile step computes.
+                    copy_ahead(t, kb[b], vb[b2]);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    step(2 * t + 1, no_loads, kb[b1], 0, vb[b], 0, kb[b1], 1, vb[b], 1, kb[b], vb[b2],
+                         vf0, kf0, sB, sA, pA, pB);
+                } else {
+                    step(2 * t + 1, with_loads, kb[b1], 0, vb[b], 0, kb[b1], 1, vb[b], 1, kb[b], vb[b2],
+                         vf0, kf0, sB, sA, pA, pB);
+                }
+                step(2 * t + 2, no_loads, kb[b1], 1, vb[b], 1, kb[b2], 0, vb[b1], 0, kb[b], vb[b2], vf0,
+                     kf0, sA, sB, pB, pA);
+            };
+            int t = 0;
+            for (; t < n_tiles; t += 3) {
+                if (2 * t + 1 > hlast + 1) break;
+                tile_step(t, 0);
+                if (t + 1 >= n_tiles) {
+                    t += 1;
+                    break;
+                }
+                if (2 * t + 3 > hlast + 1) {
+                    t += 1;
+                    break;
+                }
+                tile_step(t + 1, 1);
+                if (t + 2 >= n_tiles) {
+                    t += 2;
+                    break;
+                }
+                if (2 * t + 5 > hlast + 1) {
+                    t += 2;
+                    break;
+                }
+                tile_step(t + 2, 2);
+            }
+            for (; t < n_tiles; ++t) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                const int b = t % 3;
+                LDS3 char *kload = b == 0 ? kb[0] : b == 1 ? kb[1] : kb[2];
+                LDS3 char *vload = b == 0 ? vb[2] : b == 1 ? vb[0] : vb[1];
+                copy_ahead(t, kload, vload);
+                if constexpr (kSafeSync) {  // the second barrier of a checking tile step
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                }
+            }
+
+            // O = acc / (sum of the rounded probabilities) rounded to the element
+            // type; LSE = m * scale + ln(l) with the fp32 sum l.
+            float l_tot;
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                                 __float_as_uint(l_run), false, false);
+                l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            const float inv = 1.f / lr_run;
+            if (qrow < N) {
+                E *orow = O + ooff + (size_t)qrow * on;
+        #pragma unroll
+                for (int db = 0; db < DB; ++db)
+        #pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        f32x4 x;
+        #pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
+                        *reinterpret_cast<X4 *>(orow + 32 * db + 8 * a + 4 * g) =
+                            __builtin_convertvector(x, X4);
+                    }
+                if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
             }
         }
-        // Per pair: the three LDS reads of the pair two ahead (of the next
-        // step for the last two pairs), then each MFMA followed by its share
-        // of the softmax; the tile copies spread evenly.
-        constexpr int kValu = (56 + 2 * KS - 1) / (2 * KS);  // softmax VALU per MFMA
-        constexpr int kCopyEvery = KS / (2 * kLoads);
-#pragma unroll
-        for (int i = 0; i < KS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-            if (LOADS && i % kCopyEvery == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (__ballot(!(rs <= kSumMax<E>))) rs = rebase(sc, pc);
-        l_run += rs;
-    };
-
-    f32x16 sA, sB;
-    X8 pA[2], pB[2] = {X8{}, X8{}};
-    X8 vf0[2], kf0[2];
-    const std::integral_constant<bool, true> with_loads;
-    const std::integral_constant<bool, false> no_loads;
-
-    // Prologue: K(0), K(1), K(2), V(0), V(1) into LDS (tile step t copies
-    // K(t+3) and V(t+2)); scores of half tile 0; step 0 (whose P V^T adds
-    // zeros).
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i)
-            tile_load<D, W, STRIDED>(Kh + (size_t)i * kBc * kn, min(kBc, kv_end - i * kBc), kn, kb[i],
-                                     k_src, u, wave);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            tile_load<D, W, STRIDED>(Vh + (size_t)i * kBc * vn, min(kBc, kv_end - i * kBc), vn, vb[i],
-                                     v_src, u, wave);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    {
-        X8 kf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const LDS3 X8 *>(kb[0] + k_rd[ks]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sA[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sA = Elem<E>::mfma(kf[ks], qop[ks], sA);
-    }
-    read_pair(0, kb[0], 1, vb[0], 0, vf0[0], kf0[0]);
-    read_pair(1, kb[0], 1, vb[0], 0, vf0[1], kf0[1]);
-    // Step 0 reads K half tile 1 (tile 0, half 1); step 1 reads K tile 1
-    // half 0 and V tile 0 half 0.
-    step(0, no_loads, kb[0], 1, vb[0], 0, kb[1], 0, vb[0], 0, kb[0], vb[0], vf0, kf0, sA, sB, pB, pA);
-
-    // Tile step t (buffers b = t mod 3): step 2t+1 reads K(t+1) half 0 and
-    // V(t) half 0, step 2t+2 their halves 1, and step 2t+3 (read ahead) K(t+2)
-    // half 0 and V(t+1) half 0.  A wave whose last visible half tile hlast
-    // has had its P V^T (step hlast+1) leaves the loop; for the rest of the
-    // workgroup's tiles it only issues its share of the copies and meets the
-    // barriers.
-    const int hlast = (min(kv_end - 1, vis_max) >> 5);
-    auto tile_step = [&](int t, int b) __attribute__((always_inline)) {
-        const int b1 = (b + 1) % 3, b2 = (b + 2) % 3;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        step(2 * t + 1, with_loads, kb[b1], 0, vb[b], 0, kb[b1], 1, vb[b], 1, kb[b], vb[b2], vf0,
-             kf0, sB, sA, pA, pB);
-        step(2 * t + 2, no_loads, kb[b1], 1, vb[b], 1, kb[b2], 0, vb[b1], 0, kb[b], vb[b2], vf0,
-             kf0, sA, sB, pB, pA);
-    };
-    int t = 0;
-    for (; t < n_tiles; t += 3) {
-        if (2 * t + 1 > hlast + 1) break;
-        tile_step(t, 0);
-        if (t + 1 >= n_tiles) {
-            t += 1;
-            break;
-        }
-        if (2 * t + 3 > hlast + 1) {
-            t += 1;
-            break;
-        }
-        tile_step(t + 1, 1);
-        if (t + 2 >= n_tiles) {
-            t += 2;
-            break;
-        }
-        if (2 * t + 5 > hlast + 1) {
-            t += 2;
-            break;
-        }
-        tile_step(t + 2, 2);
-    }
-    for (; t < n_tiles; ++t) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const E *kbase = Kh + (size_t)(t + 3) * kBc * kn;
-        const E *vbase = Vh + (size_t)(t + 2) * kBc * vn;
-        const int krows = min(kBc, kv_end - (t + 3) * kBc);
-        const int vrows = min(kBc, kv_end - (t + 2) * kBc);
-        const int b = t % 3;
-        LDS3 char *kload = b == 0 ? kb[0] : b == 1 ? kb[1] : kb[2];
-        LDS3 char *vload = b == 0 ? vb[2] : b == 1 ? vb[0] : vb[1];
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            tile_load<D, W, STRIDED>(kbase, krows, kn, kload, k_src, u, wave);
-            tile_load<D, W, STRIDED>(vbase, vrows, vn, vload, v_src, u, wave);
-        }
-    }
-
-    // O = acc / l rounded to the element type; LSE = m * scale + ln(l).
-    float l_tot;
-    {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
-                                                         __float_as_uint(l_run), false, false);
-        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    const float inv = 1.f / l_tot;
-    if (qrow < N) {
-        E *orow = O + ooff + (size_t)qrow * on;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                f32x4 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
-                *reinterpret_cast<X4 *>(orow + 32 * db + 8 * a + 4 * g) =
-                    __builtin_convertvector(x, X4);
-            }
-        if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
     }
 }
 
@@ -1015,29 +1161,68 @@ constexpr int kPipeWaves = 8;
 constexpr int kPipeWaves64 = 4;
 constexpr int kPipeMinN64 = 8192;
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The launch of fwd_pipe_kernel.  W = 8 (96 KiB of LDS, one workgroup per
+// compute unit): persistent, one workgroup per compute unit, at most one per
+// work unit (modes 0-2).  W = 4: one workgroup per tile (mode 3); the
+// persistent form measured 6 % slower there (B1 H16 N16384 d64 causal, same
+// box), as two workgroups of one wave per SIMD share a compute unit and run
+// unequal tiles side by side.
+template <typename E, int D, bool CAUSAL, bool STRIDED, int W>
+hipError_t launch_pipe(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                       int H, int N, float scale, float scale_log2, const FwdStrides &st,
+                       hipStream_t stream) {
+    constexpr int kRows = W * kRowsPerWave;
+    const int nqt = (N + kRows - 1) / kRows;
+    const int n_bh = B * H;
+    const long n_tiles = (long)n_bh * nqt;
+    int mode = 3;
+    long grid = n_tiles;
+    if (W == 8) {
+        const long slots = device_cus();
+        const long n_pairs = (long)n_bh * ((nqt + 1) / 2);
+        mode = 0;
+        if (n_tiles >= slots && slots % 8 == 0 && n_bh % 8 == 0)
+            mode = 2;
+        else if (CAUSAL && n_pairs >= slots)
+            mode = 1;
+        const long n_units = mode == 1 ? n_pairs : n_tiles;
+        grid = n_units < slots ? n_units : slots;
+    }
+    hipLaunchKernelGGL((fwd_pipe_kernel<E, D, CAUSAL, STRIDED, W>), dim3((int)grid), dim3(64 * W),
+                       0, stream, static_cast<const E *>(q), static_cast<const E *>(k),
+                       static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, n_bh, mode,
+                       scale, scale_log2, st);
+    return hipGetLastError();
+}
+
 template <typename E, int D, bool CAUSAL, bool STRIDED>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                   int N, float scale, const FwdStrides &st, hipStream_t stream) {
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if constexpr (D == 128) {
-        constexpr int kRows = kPipeWaves * kRowsPerWave;
-        const int nqt = (N + kRows - 1) / kRows;
-        hipLaunchKernelGGL((fwd_pipe_kernel<E, D, CAUSAL, STRIDED, kPipeWaves>), dim3(B * H * nqt),
-                           dim3(64 * kPipeWaves), 0, stream, static_cast<const E *>(q),
-                           static_cast<const E *>(k), static_cast<const E *>(v),
-                           static_cast<E *>(o), lse, N, nqt, scale, scale_log2, st);
+        return launch_pipe<E, D, CAUSAL, STRIDED, kPipeWaves>(q, k, v, o, lse, B, H, N, scale,
+                                                              scale_log2, st, stream);
     } else {
         if constexpr (D == 64 && CAUSAL) {
-            if (N >= kPipeMinN64) {
-                constexpr int kRows = kPipeWaves64 * kRowsPerWave;
-                const int nqt = (N + kRows - 1) / kRows;
-                hipLaunchKernelGGL((fwd_pipe_kernel<E, D, CAUSAL, STRIDED, kPipeWaves64>),
-                                   dim3(B * H * nqt), dim3(64 * kPipeWaves64), 0, stream,
-                                   static_cast<const E *>(q), static_cast<const E *>(k),
-                                   static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt,
-                                   scale, scale_log2, st);
-                return hipGetLastError();
-            }
+            if (N >= kPipeMinN64)
+                return launch_pipe<E, D, CAUSAL, STRIDED, kPipeWaves64>(q, k, v, o, lse, B, H, N,
+                                                                        scale, scale_log2, st,
+                                                                        stream);
         }
         const int nqt = (N + kBr - 1) / kBr;
         hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(B * H * nqt), dim3(kThreads),

@@ -5,7 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// FA_SAFE_SYNC=1 builds a checking variant of the library: every copy into
+// an LDS tile buffer is completed and made visible by a workgroup barrier
+// before any wave computes on, and every buffer's reads complete at a barrier
+// before it is refilled.  Its results must equal the regular build's bit for
+// bit (the arithmetic is unchanged; only the overlap of copies and compute
+// goes); a difference would show a missing wait or barrier in the regular
+// pipelines.
+#ifndef FA_SAFE_SYNC
+#define FA_SAFE_SYNC 0
+#endif
+
 namespace fa {
+
+constexpr bool kSafeSync = FA_SAFE_SYNC != 0;
 
 // Each launcher enqueues one kernel on `stream` and returns the launch status
 // (hipGetLastError).  Arguments have already been validated by fa_api.cpp.

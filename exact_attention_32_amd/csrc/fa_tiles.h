@@ -43,6 +43,9 @@ struct TileOps<__bf16> {
     static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
 };
 template <>
 struct TileOps<_Float16> {
@@ -51,7 +54,27 @@ struct TileOps<_Float16> {
     static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
 };
+
+// 0/1 selector for row sums of P^T operands on the matrix core: with it as
+// the A operand of a 16 x 16 x 32 MFMA whose B operand is a P^T operand of
+// O^T += V^T P^T (lane l: query l % 32, keys 8(l / 32) .. +7 of a 16-key
+// step), every lane's four outputs hold the 16-key sum of its own query.  (The
+// B operand is read as column l % 16, reduction index 8(l / 16) .. +7, so lane
+// groups 0, 2 carry query n and groups 1, 3 query n + 16; row m selects
+// reduction group k / 8 when (m / 4) and (k / 8) have the same parity, and the
+// output lane l holds column l % 16, rows 4(l / 16) .. +3.)
+template <typename E>
+__device__ __forceinline__ typename TileOps<E>::x8 rowsum_selector(int lane) {
+    typename TileOps<E>::x8 a;
+    const float one = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (E)one;
+    return a;
+}
 
 // One swizzle for tiles read both by 128-bit row reads (16 rows x one 16-byte
 // chunk per LDS pass) and by the 64-bit transpose read (4 rows x 4 chunks per

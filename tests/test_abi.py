@@ -31,6 +31,15 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"{name} missing from {fa.LIB_PATH}"
 
 
+def test_checking_build_exports_every_declared_symbol():
+    """The checking build (FA_SAFE_SYNC=1) is the same library: same ABI."""
+    from exact_attention_32_amd import _lib
+
+    safe = _lib.open_library(_lib.SAFE_SYNC_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(safe, name), f"{name} missing from {_lib.SAFE_SYNC_LIB_PATH}"
+
+
 def test_status_codes_match_header():
     text = open(os.path.join(ROOT, "include", "fa.h")).read()
     codes = dict((n, int(v)) for n, v in re.findall(r"\b(FA_\w+)\s*=\s*(\d+)", text))
