@@ -4,7 +4,8 @@ O = softmax(scale * Q K^T [+ causal mask]) V and the per-row log-sum-exp,
 and the gradients dQ, dK, dV, computed tile by tile in hand-written HIP
 kernels behind the C ABI of ``include/fa.h``.  This package is the thin Python
 binding of that library (``fa_fwd``, ``fa_fwd_ex``, ``fa_fwd_f32``, ``fa_fwd_kv_outer``,
-``fa_bwd``, ``fa_bwd_ex``, ``fa_decode``, ``fa_decode_ex`` and their workspace-size queries, ``fa_strerror``,
+``fa_bwd``, ``fa_bwd_ex``, ``fa_decode``, ``fa_decode_ex``, ``fa_decode_noalloc`` and the
+workspace-size queries, ``fa_strerror``,
 with the C names, plus the torch conveniences ``forward``,
 ``forward_kv_outer``, ``backward`` and ``decode``) and the seeded input
 generators in ``inputs``.
@@ -22,7 +23,9 @@ from ._lib import (  # noqa: F401
     FA_ERR_DTYPE,
     FA_ERR_SHAPE,
     FA_ERR_STRIDE,
+    FA_ERR_SCRATCH,
     FA_ERR_WORKSPACE,
+    FA_DECODE_SCRATCH_BYTES,
     FA_OK,
     LIB_PATH,
     FAError,
@@ -32,6 +35,7 @@ from ._lib import (  # noqa: F401
     fa_bwd_ex,
     fa_decode,
     fa_decode_ex,
+    fa_decode_noalloc,
     fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_ex,

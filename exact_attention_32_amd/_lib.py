@@ -27,10 +27,14 @@ FA_ERR_ALIAS = 7
 FA_ERR_WORKSPACE = 8
 FA_ERR_DTYPE = 9
 FA_ERR_STRIDE = 10
+FA_ERR_SCRATCH = 11
+# bytes of the fixed device scratch of fa_decode_noalloc (include/fa.h)
+FA_DECODE_SCRATCH_BYTES = 17 << 20
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_ex", "fa_decode_workspace_size",
+EXPORTS = ("fa_bwd", "fa_bwd_ex", "fa_decode", "fa_decode_ex", "fa_decode_noalloc",
+           "fa_decode_workspace_size",
            "fa_fwd", "fa_fwd_ex", "fa_fwd_f32", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_size",
            "fa_strerror")
 
@@ -75,6 +79,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa_decode_ex.restype = i
     lib.fa_decode_ex.argtypes = ([i] + [vp] * 5 + [i] * 5 + [f, i, i, vp, ctypes.c_size_t,
                                                              ctypes.POINTER(ctypes.c_int64), vp])
+    lib.fa_decode_noalloc.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp] * 5 + [i] * 5 + [f, i, i, vp]
     lib.fa_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_decode_workspace_size.argtypes = [i] * 6
     lib.fa_fwd_ex.restype = i
@@ -210,6 +216,17 @@ def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, works
                                         int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
                                         int(bool(causal)), int(num_splits), _ptr(workspace),
                                         int(workspace_bytes), _stream(stream)))
+
+
+def fa_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
+                      stream=None) -> int:
+    """Enqueue fa_decode with the library's fixed scratch instead of a
+    workspace (nothing is allocated).  Returns the fa_status code
+    (FA_ERR_SCRATCH when the partials exceed FA_DECODE_SCRATCH_BYTES)."""
+    return int(load_library().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                int(B), int(H), int(Nq), int(Nk), int(d),
+                                                float(scale), int(bool(causal)), int(num_splits),
+                                                _stream(stream)))
 
 
 def fa_decode_ex(dtype, q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits, workspace,

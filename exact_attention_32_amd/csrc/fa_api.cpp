@@ -322,6 +322,40 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                      int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                      hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 1 || Nq > fa::kDecodeMaxQueries || Nk < Nq || Nk > (1 << 30))
+        return FA_ERR_SHAPE;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    uint64_t lse_off = 0;
+    const uint64_t need = decode_workspace(B, H, Nq, d, S, &lse_off);
+    if (need > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+    for (const void *p : {q, k, v, (const void *)o, (const void *)lse})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return FA_ERR_ALIGN;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    const uint64_t q_bytes = bh * Nq * d * 2, kv_bytes = bh * (uint64_t)Nk * d * 2;
+    const uint64_t l_bytes = bh * Nq * 4;
+    struct Span { const void *p; uint64_t n; };
+    const Span ins[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
+    const Span outs[] = {{o, q_bytes}, {lse, l_bytes}};
+    for (const Span &w : outs)
+        for (const Span &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_ALIAS;
+    if (overlaps(o, q_bytes, lse, l_bytes)) return FA_ERR_ALIAS;
+    void *scratch = nullptr;
+    if (fa::decode_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+    float *o_part = static_cast<float *>(scratch);
+    float *lse_part = reinterpret_cast<float *>(static_cast<char *>(scratch) + lse_off);
+    const hipError_t e = fa::launch_decode_bf16(q, k, v, o, lse, B, H, Nq, Nk, d, scale,
+                                                causal != 0, S, o_part, lse_part, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_decode_ex(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
                  int B, int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
                  void *workspace, size_t workspace_bytes, const int64_t *strides,
@@ -381,6 +415,7 @@ const char *fa_strerror(int status) {
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL or smaller than required";
         case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_BF16 or FA_DTYPE_FP16";
         case FA_ERR_STRIDE: return "FA_ERR_STRIDE: strides must be >= 0, row strides in [d, 2^24], output rows disjoint";
+        case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the partials of this call exceed the fixed scratch of fa_decode_noalloc (FA_DECODE_SCRATCH_BYTES); pass a smaller num_splits";
         default: return "unknown fa status code";
     }
 }

@@ -31,6 +31,8 @@
 // two-block rule at the end.  K and V rows go straight from HBM into
 // registers (each row is used by one wave only, so LDS would add nothing).
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stdint.h>
 
 #include <cmath>
@@ -721,6 +723,34 @@ hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float 
 }
 
 }  // namespace
+
+// Fixed scratch of the allocation-free decode entry point (fa_decode_noalloc):
+// the split kernel's fp32 partials live here instead of in a caller workspace.
+// Each device holds its own copy for the life of the process; host code must
+// use the device address from hipGetSymbolAddress, never this name.
+static __device__ __align__(256) unsigned char decode_scratch_mem[kDecodeScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void **ptr) {
+    *ptr = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(decode_scratch_mem));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                               int B, int H, int Nq, int Nk, int d, float scale, bool causal,

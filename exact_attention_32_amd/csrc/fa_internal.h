@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa.h"
+
 // FA_SAFE_SYNC=1 builds a checking variant of the library: every copy into
 // an LDS tile buffer is completed and made visible by a workgroup barrier
 // before any wave computes on, and every buffer's reads complete at a barrier
@@ -61,6 +63,14 @@ hipError_t launch_fwd_kvouter_bf16(const void *q, const void *k, const void *v, 
 
 // Decode (few queries over many keys, key axis split in chunks).
 constexpr int kDecodeMaxQueries = 16;
+// Bytes of the fixed device scratch of fa_decode_noalloc (the partial outputs
+// and LSEs of the automatic split count at B2 H32 Nq16 d128 fit).
+constexpr unsigned long kDecodeScratchBytes = FA_DECODE_SCRATCH_BYTES;
+static_assert(kDecodeScratchBytes % 256 == 0, "scratch size");
+constexpr int kMaxDevices = 64;
+// Device address of the current device's copy of that scratch (looked up
+// once per device with hipGetSymbolAddress).
+hipError_t decode_scratch(void **ptr);
 constexpr int kDecodeMinChunk = 64;       // keys per chunk, at least
 constexpr int kDecodeTargetWaves = 2048;  // single-wave workgroups aimed for
 // Number of chunks for a requested count (<= 0: automatic).

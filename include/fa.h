@@ -68,9 +68,13 @@ enum fa_status {
     FA_ERR_ALIAS = 7,    /* an output overlaps an input or another output    */
     FA_ERR_WORKSPACE = 8,/* workspace NULL or smaller than required          */
     FA_ERR_DTYPE = 9,    /* unknown element type                             */
-    FA_ERR_STRIDE = 10   /* strides invalid (row stride < d or > 2^24,       */
+    FA_ERR_STRIDE = 10,  /* strides invalid (row stride < d or > 2^24,       */
                          /* negative, or an output whose rows overlap)       */
+    FA_ERR_SCRATCH = 11  /* fa_decode_noalloc: partials exceed its scratch   */
 };
+
+/* Bytes of the fixed device scratch of fa_decode_noalloc. */
+#define FA_DECODE_SCRATCH_BYTES (17ul << 20)
 
 /* Element types of fa_fwd_ex. */
 enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
@@ -171,6 +175,30 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
 /* Bytes of workspace fa_decode needs for these arguments (0 if they are
  * invalid shapes). */
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument; the fp32 partials go to a fixed
+ * scratch array that the library holds in device memory, one per GPU, of
+ * FA_DECODE_SCRATCH_BYTES (17 MiB) for the life of the process.  The call
+ * allocates nothing and makes no allocating runtime call.
+ *
+ * Arguments, layout and results as for fa_decode (same kernels, same
+ * num_splits rule); a call whose partials, fa_decode_workspace_size(B, H,
+ * Nq, Nk, d, num_splits) bytes, exceed FA_DECODE_SCRATCH_BYTES returns
+ * FA_ERR_SCRATCH before anything is enqueued (pass a smaller num_splits).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (on different streams, or from different threads without
+ * ordering) race on it and must not be issued; calls ordered on one stream
+ * are safe.  The scratch needs no clearing (the split kernel writes every
+ * partial it reads back).  Errors as for fa_decode with FA_ERR_SCRATCH in
+ * place of FA_ERR_WORKSPACE; FA_ERR_HIP also if the scratch's device address
+ * cannot be obtained.
+ */
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int num_splits, hipStream_t stream);
 
 /*
  * fa_decode_ex -- fa_decode generalised the way fa_fwd_ex generalises

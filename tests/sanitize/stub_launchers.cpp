@@ -43,4 +43,9 @@ hipError_t launch_decode_ex(bool, const void *, const void *, const void *, void
     return hipErrorInvalidValue;
 }
 
+hipError_t decode_scratch(void **ptr) {
+    *ptr = nullptr;
+    return hipErrorInvalidValue;
+}
+
 }  // namespace fa

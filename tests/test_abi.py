@@ -48,12 +48,12 @@ def test_status_codes_match_header():
 
 
 def test_strerror(lib):
-    for code in range(11):
+    for code in range(12):
         s = fa.fa_strerror(code)
         assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM",
                              "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP",
                              "FA_ERR_ALIAS", "FA_ERR_WORKSPACE", "FA_ERR_DTYPE",
-                             "FA_ERR_STRIDE"][code])
+                             "FA_ERR_STRIDE", "FA_ERR_SCRATCH"][code])
     assert "unknown" in fa.fa_strerror(99)
     assert "unknown" in fa.fa_strerror(-1)
 
@@ -200,6 +200,37 @@ def test_decode_validation_codes(lib):
     assert call(ws=DK) == fa.FA_ERR_ALIAS
     assert call(o=DQ) == fa.FA_ERR_ALIAS
     assert call(lse=DW + 64) == fa.FA_ERR_ALIAS
+
+
+def test_decode_noalloc_validation_codes(lib):
+    """The allocation-free decode rejects bad arguments like fa_decode, and
+    calls whose partials exceed its fixed scratch with FA_ERR_SCRATCH, all
+    before any HIP call (the scratch size check comes before the device
+    address lookup)."""
+    DQ, DK, DV, DO, DL = (BASE + i * GAP for i in range(5))
+
+    def call(q=DQ, k=DK, v=DV, o=DO, lse=DL, B=2, H=3, Nq=1, Nk=500, d=128, scale=0.125,
+             causal=0, splits=0):
+        return fa.fa_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, splits, None)
+    assert call(q=0) == fa.FA_ERR_NULL
+    assert call(lse=0) == fa.FA_ERR_NULL
+    assert call(Nq=0) == fa.FA_ERR_SHAPE
+    assert call(Nq=17) == fa.FA_ERR_SHAPE
+    assert call(Nq=8, Nk=7) == fa.FA_ERR_SHAPE
+    assert call(d=72) == fa.FA_ERR_HEADDIM
+    assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    # partials of B64 H64 Nq16 d128 with the automatic split count: far past the scratch
+    assert fa.fa_decode_workspace_size(64, 64, 16, 8192, 128, 0) > fa.FA_DECODE_SCRATCH_BYTES
+    assert call(B=64, H=64, Nq=16, Nk=8192) == fa.FA_ERR_SCRATCH
+    assert call(B=64, H=64, Nq=16, Nk=8192, splits=1) == fa.FA_ERR_SCRATCH
+    # the largest automatic case it is sized for fits
+    assert fa.fa_decode_workspace_size(2, 32, 16, 8192, 128, 0) <= fa.FA_DECODE_SCRATCH_BYTES
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_DECODE_SCRATCH_BYTES \((\d+)ul << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_DECODE_SCRATCH_BYTES
+    assert call(B=2, H=32, Nq=16, Nk=8192, o=DO + 8) == fa.FA_ERR_ALIGN
+    assert call(o=DQ) == fa.FA_ERR_ALIAS
+    assert call(lse=DO + 64) == fa.FA_ERR_ALIAS
 
 
 def test_kv_outer_validation_and_size(lib):
