@@ -42,7 +42,7 @@ Counter helpers (used to produce the summaries under profiles/):
                                            of 1 GiB (for counter scaling)
   python bench.py --summarize-trace DIR CMD       per-kernel summary of a
                                                   --kernel-trace --stats run
-  python bench.py --summarize-counters FDIR WDIR WORKLOAD CMD
+  python bench.py --summarize-counters FDIR WDIR WORKLOAD CMD [KERNEL]
                                                   traffic summary of the
                                                   FETCH_SIZE / WRITE_SIZE runs
   python bench.py --summarize-pmc KERNEL_SUBSTRING TRACE_DIR CMD DIR [DIR ...]
@@ -71,7 +71,6 @@ KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_fwd_bf16.hip",
                   "exact_attention_32_amd/csrc/fa_fwd_f32.hip"]
 BWD_KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_bwd_bf16.hip"]
 COPY_BYTES = 1 << 30
-TRAFFIC_FILE = "profiles/fa_fwd_bf16_b2h32n8192d128_causal_traffic.txt"
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -90,24 +89,24 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
 
 
 def read_traffic(workload: str):
-    """Bytes per launch from the committed counter summary, or None when the
-    summary is for another workload or an older kernel source."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if ":" in line and line.split(":", 1)[0].isupper():
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
-    if fields.get("WORKLOAD") != workload:
-        return None
-    if fields.get("KERNEL_SOURCE_SHA256_16") != kernel_source_hash():
-        return None
-    try:
-        return int(fields["HBM_BYTES_PER_LAUNCH"])
-    except (KeyError, ValueError):
-        return None
+    """Bytes per launch from the committed counter summary of this workload
+    (profiles/*_traffic.txt), or None when there is none for the current
+    kernel source."""
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.txt"))):
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.split(":", 1)[0].isupper():
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("WORKLOAD") != workload:
+            continue
+        if fields.get("KERNEL_SOURCE_SHA256_16") != kernel_source_hash():
+            continue
+        try:
+            return int(fields["HBM_BYTES_PER_LAUNCH"])
+        except (KeyError, ValueError):
+            continue
+    return None
 
 
 def cpu_model() -> str:
@@ -263,16 +262,18 @@ def summarize_trace(directory: str, command: str) -> None:
         print(f"resources {name}: vgpr={vgpr} agpr={agpr} sgpr={sgpr} lds={lds} scratch={scratch}")
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> None:
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str,
+                       kernel: str = "fwd_") -> None:
     """Print the traffic summary of two `rocprofv3 --pmc` runs of
     `bench.py --copy-calibration` (FETCH_SIZE in `fetch_dir`, WRITE_SIZE in
-    `write_dir`).  Each counter is scaled by COPY_BYTES / (its reading for
-    the plain device copy of COPY_BYTES that the same run performs)."""
+    `write_dir`) for the kernels whose name contains `kernel`.  Each counter
+    is scaled by COPY_BYTES / (its reading for the plain device copy of
+    COPY_BYTES that the same run performs)."""
     q = "select kernel_name, value from counters_collection where counter_name = '%s'"
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _db_rows(d, q % counter)
-        fa_kib = [v for k, v in rows if "fwd_kernel" in k or "fwd_pipe_kernel" in k]
+        fa_kib = [v for k, v in rows if kernel in k]
         copy_kib = [v for k, v in rows if "copyBuffer" in k]
         if not fa_kib or len(copy_kib) != 1:
             raise SystemExit(f"{counter}: expected attention launches and one copy in {d}")
@@ -281,6 +282,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
         out[counter] = (mean, factor, fa_kib, copy_kib[0])
     print(f"COMMAND: {command}")
     print(f"WORKLOAD: {workload}")
+    print(f"KERNEL: {kernel}")
     print(f"KERNEL_SOURCE_SHA256_16: {kernel_source_hash()}")
     total = 0
     for counter, (mean, factor, vals, copy) in out.items():
@@ -471,8 +473,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
-    ap.add_argument("--summarize-counters", nargs=4,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "WORKLOAD", "COMMAND"))
+    ap.add_argument("--summarize-counters", nargs="+",
+                    metavar="ARG", help="FETCH_DIR WRITE_DIR WORKLOAD COMMAND [KERNEL_SUBSTRING]")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG")
     ap.add_argument("--oracle-timings", action="store_true",
                     help="time the oracle on the small workloads on one core and on all "
@@ -490,7 +492,7 @@ def main() -> int:
         summarize_trace(*args.summarize_trace)
         return 0
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters[:5])
         return 0
     if args.summarize_pmc:
         a = args.summarize_pmc

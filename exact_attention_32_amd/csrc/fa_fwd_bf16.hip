@@ -241,6 +241,72 @@ __device__ __forceinline__ void map_block(int L, int W, int nqt, bool causal, in
     if (causal) qt = nqt - 1 - qt;
 }
 
+// Static schedules of the forward kernels.  Work item `it` of this
+// workgroup: returns 0 when the workgroup has no more items, 1 with (bh, qt)
+// set, 2 for a hole to skip.  Workgroup w runs on XCD w mod 8 (workgroups are
+// dealt round-robin over the XCDs).  G = gridDim.x.
+//  * mode 3: one tile per workgroup, the grid covering every tile, mapped by
+//    map_block (the dispatcher balances the workgroups).
+//  * mode 2 (persistent; the grid and the heads divide by 8): XCD x owns heads
+//    x, x+8, ...; its L = G/8 workgroups take its (head, tile) items in rounds
+//    of L, head-major with the longest causal tiles first, in snake order
+//    (round r: workgroup lw takes item rL + lw, or rL + L-1-lw when r is odd).
+//    Causal costs fall linearly along a head, so two consecutive rounds give
+//    every workgroup the same work, and an XCD works on about one head at a
+//    time, whose K/V its L2 then serves.
+//  * mode 1 (persistent, causal): units are the tile pairs (nqt-1-i, i) of a
+//    head, equal in cost, taken round-robin.
+//  * mode 0 (persistent): single tiles round-robin, longest causal tiles
+//    first over all heads.
+// No atomics and no dispatcher involvement after the launch in modes 0-2.
+__device__ __forceinline__ int sched_item(int mode, int it, int n_bh, int nqt, bool causal,
+                                          int by_cost_below, int &bh, int &qt) {
+    const int G = gridDim.x;
+    if (mode == 3) {
+        if (it > 0) return 0;
+        map_block(blockIdx.x, G, nqt, causal, by_cost_below, bh, qt);
+        return 1;
+    }
+    const int L = G >> 3;
+    const int x = blockIdx.x & 7, lw = blockIdx.x >> 3;
+    if (mode == 2) {
+        const int n_local = (n_bh >> 3) * nqt;
+        if (it * L >= n_local) return 0;
+        const int pos = it * L + ((it & 1) ? (L - 1 - lw) : lw);
+        if (pos >= n_local) return 2;
+        const int lh = pos / nqt, pq = pos - lh * nqt;
+        bh = lh * 8 + x;
+        qt = causal ? nqt - 1 - pq : pq;
+        return 1;
+    }
+    const int slot = ((G & 7) == 0) ? x * L + lw : (int)blockIdx.x;
+    if (mode == 1) {
+        const int npairs = (nqt + 1) / 2;
+        const int unit = slot + (it >> 1) * G;
+        if (unit >= n_bh * npairs) return 0;
+        bh = unit / npairs;
+        const int pi = unit - bh * npairs;
+        if (it & 1) {
+            if (nqt - 1 - pi == pi) return 2;  // the middle tile of an odd count
+            qt = pi;
+        } else {
+            qt = nqt - 1 - pi;
+        }
+        return 1;
+    }
+    const int unit = slot + it * G;
+    if (unit >= n_bh * nqt) return 0;
+    if (causal) {
+        const int rank = unit / n_bh;
+        bh = unit - rank * n_bh;
+        qt = nqt - 1 - rank;
+    } else {
+        bh = unit / nqt;
+        qt = unit - bh * nqt;
+    }
+    return 1;
+}
+
 __device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
@@ -301,8 +367,8 @@ struct FwdStrides {
 template <typename E, int DH, bool CAUSAL, bool STRIDED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
-           E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, float scale,
-           float scale_log2, FwdStrides st) {
+           E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int n_bh, int mode,
+           float scale, float scale_log2, FwdStrides st) {
     typedef typename Elem<E>::x8 X8;
     typedef typename Elem<E>::x4 X4;
     static_assert(DH % 16 == 0 && DH >= 16 && DH <= 128, "head dim");
@@ -329,43 +395,15 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
     const int g = lane >> 5;  // half-wave
     const int j = lane & 31;  // query column of this lane (S^T / O^T layouts)
 
-    int bh, qt;
-    map_block(blockIdx.x, gridDim.x, nqt, CAUSAL, 64, bh, qt);  // 2-3 workgroups per CU
-    const int r0 = qt * kBr;
-    size_t qoff, koff, voff, ooff;
-    int qn, kn, vn, on;
+    int qn, kn, vn, on;  // row strides (elements)
     if constexpr (STRIDED) {
-        const int b = bh / st.H, h = bh - b * st.H;
-        qoff = (size_t)(b * st.qb + h * st.qh);
-        koff = (size_t)(b * st.kb + h * st.kh);
-        voff = (size_t)(b * st.vb + h * st.vh);
-        ooff = (size_t)(b * st.ob + h * st.oh);
         qn = st.qn;
         kn = st.kn;
         vn = st.vn;
         on = st.on;
     } else {
-        qoff = koff = voff = ooff = (size_t)bh * (size_t)N * DH;
         qn = kn = vn = on = DH;
     }
-    const E *Qh = Q + qoff;
-    const E *Kh = K + koff;
-    const E *Vh = V + voff;
-    const int wrow0 = r0 + wave * kRowsPerWave;
-    const int qrow = wrow0 + j;
-
-    // Q^T as the B operand: lane (g, j) holds query qrow, columns 16ks+8g..+7.
-    X8 qop[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
-        qop[ks] = __builtin_bit_cast(X8, x);
-    }
-
-    const int kv_end = CAUSAL ? min(N, r0 + kBr) : N;
-    const int n_tiles = (kv_end + kBc - 1) / kBc;
-
     // ---- staging offsets (lane constants) ---------------------------------
     // Load u of wave w fills LDS chunk positions [(u*kWaves + w)*64, +64); lane l
     // fills position q = that base + l, i.e. row q / kChunksPerRow, stored
@@ -410,224 +448,266 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
         v_rd[db] = (uint32_t)(row * D * 2 + ((c ^ v_swz<D>(row)) << 4) + ((col & 4) << 1));
     }
 
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m_run = -INFINITY;  // exponent base of row qrow (raw score units)
-    float mc_run = -INFINITY; // the base in scaled log2 units (m_run * scale_log2)
-    float l_run = 0.f;        // this half-wave's share of the running sum
-    float lr_run = 0.f;       // running sum of the rounded probabilities (whole row)
     const X8 sel = rowsum_selector<E>(lane);
-
     LDS3 char *const k0 = (LDS3 char *)lds_k0;
     LDS3 char *const k1 = (LDS3 char *)lds_k1;
     LDS3 char *const v0 = (LDS3 char *)lds_v0;
     LDS3 char *const v1 = (LDS3 char *)lds_v1;
 
-    // One key tile: prefetch the next tile into the other buffers, then
-    // S^T, softmax and O^T on this one.
-    auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk,
-                    LDS3 char *nv) {
-        const int c0 = t * kBc;
-        const bool prefetch = t + 1 < n_tiles;
-        auto load = [&](int i) __attribute__((always_inline)) {
-            issue_tile_load<DH, kLoads, STRIDED>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src,
-                                                 wave, kn, vn);
-        };
-
-        // Checking build: the next tile is copied and visible before this
-        // tile's compute starts (its buffers were released at the barrier
-        // that ended the previous tile).
-        if constexpr (kSafeSync) {
-            if (prefetch) {
-#pragma unroll
-                for (int i = 0; i < 2 * kLoads; ++i) load(i);
-            }
+    // Work items: see sched_item (mode 3: one tile, from map_block).
+    for (int it = 0;; ++it) {
+        int bh, qt;
+        const int got = sched_item(mode, it, n_bh, nqt, CAUSAL, 64, bh, qt);
+        if (got == 0) break;
+        if (got == 2) continue;
+        {
+            // The previous tile's LDS buffers are free and its copies landed.
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-        }
-        // A wave whose rows all precede this tile has nothing to add.
-        const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
-        if (!active && prefetch && !kSafeSync) {
-#pragma unroll
-            for (int i = 0; i < 2 * kLoads; ++i) load(i);
-        }
-        if (active) {
+            const int r0 = qt * kBr;
+            size_t qoff, koff, voff, ooff;
+            if constexpr (STRIDED) {
+                const int b = bh / st.H, h = bh - b * st.H;
+                qoff = (size_t)(b * st.qb + h * st.qh);
+                koff = (size_t)(b * st.kb + h * st.kh);
+                voff = (size_t)(b * st.vb + h * st.vh);
+                ooff = (size_t)(b * st.ob + h * st.oh);
+            } else {
+                qoff = koff = voff = ooff = (size_t)bh * (size_t)N * DH;
+            }
+            const E *Qh = Q + qoff;
+            const E *Kh = K + koff;
+            const E *Vh = V + voff;
+            const int wrow0 = r0 + wave * kRowsPerWave;
+            const int qrow = wrow0 + j;
 
-            // S^T[key][query] = K Q^T for the kBc keys of this tile.
-            f32x16 s[kBc / 32];
-#pragma unroll
-            for (int kb = 0; kb < kBc / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            // All K fragments of the tile are requested before the first MFMA,
-            // so the LDS latency is paid once per tile, not once per k-step.
-            X8 kf[KS][kBc / 32];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < kBc / 32; ++kb)
-                    kf[ks][kb] = *reinterpret_cast<const LDS3 X8 *>(
-                        kt + k_rd[ks] + kb * 32 * D * 2);
-            __builtin_amdgcn_sched_barrier(0);
-            // The S MFMAs run at raised wave priority: the other wave on this
-            // SIMD (from another workgroup) then tends to run its softmax while
-            // this one keeps the matrix core busy, instead of both waves
-            // alternating instruction by instruction through the same phase.
-            __builtin_amdgcn_s_setprio(1);
-            // The next tile's loads go out one per k-step, between the MFMAs.
-#pragma unroll
+            // Q^T as the B operand: lane (g, j) holds query qrow, columns 16ks+8g..+7.
+            X8 qop[KS];
+        #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < kBc / 32; ++kb)
-                    s[kb] = Elem<E>::mfma(kf[ks][kb], qop[ks], s[kb]);
-                if (prefetch && !kSafeSync) {
-#pragma unroll
-                    for (int i = ks * kTileLoads / KS; i < (ks + 1) * kTileLoads / KS; ++i) load(i);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (qrow < N) x = load16(Qh + (size_t)qrow * qn + 16 * ks + 8 * g);
+                qop[ks] = __builtin_bit_cast(X8, x);
             }
 
-            __builtin_amdgcn_s_setprio(0);
+            const int kv_end = CAUSAL ? min(N, r0 + kBr) : N;
+            const int n_tiles = (kv_end + kBc - 1) / kBc;
 
-            // All V^T fragments of the tile are requested now; the softmax below
-            // covers their latency.  Fragment (T, db) is two transpose reads
-            // (keys 16T+4g+k and 16T+8+4g+k, columns of d-block db).
-            X8 vf[kBc / 16][D / 32];
-#pragma unroll
-            for (int T = 0; T < kBc / 16; ++T)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const LDS3 char *base = vt + v_rd[db] + T * 16 * D * 2;
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base));
-                    const v4i16 hi =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
-                    vf[T][db] = __builtin_bit_cast(
-                        X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                }
+            f32x16 acc[D / 32];
+        #pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+        #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+            float m_run = -INFINITY;  // exponent base of row qrow (raw score units)
+            float mc_run = -INFINITY; // the base in scaled log2 units (m_run * scale_log2)
+            float l_run = 0.f;        // this half-wave's share of the running sum
+            float lr_run = 0.f;       // running sum of the rounded probabilities (whole row)
 
-            // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
-            const bool need_mask = (CAUSAL && c0 + kBc - 1 > wrow0) || (c0 + kBc > N);
-            if (need_mask) {
-                // visible iff 32kb + 8(r/4) + r%4 <= lim, lim = min(qrow, N-1) - c0 - 4g
-                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - c0 - 4 * g;
-#pragma unroll
-                for (int kb = 0; kb < kBc / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
-            }
 
-            // Fast path: probabilities against the current exponent base, with
-            // no row maximum.  The tile is accepted when every half-row sum is
-            // at most kSumMax (so every probability is); the test also rejects
-            // inf / NaN sums, in particular on the first tile, whose base is
-            // still -inf.  Numerator and denominator share the base, so
-            // O = acc / l and LSE = base*scale + ln(l) do not depend on where
-            // the base sits.
-            X8 pop[kBc / 16];
-            float rs = 0.f;
-            auto exps = [&](float mcx) __attribute__((always_inline)) {
-                rs = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < kBc / 32; ++kb) {
-                    f32x8 lo, hi;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -mcx));
-                        hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 8], scale_log2, -mcx));
-                        rs += lo[r];
-                        rs += hi[r];
+            // One key tile: prefetch the next tile into the other buffers, then
+            // S^T, softmax and O^T on this one.
+            auto step = [&](int t, const LDS3 char *kt, const LDS3 char *vt, LDS3 char *nk,
+                            LDS3 char *nv) {
+                const int c0 = t * kBc;
+                const bool prefetch = t + 1 < n_tiles;
+                auto load = [&](int i) __attribute__((always_inline)) {
+                    issue_tile_load<DH, kLoads, STRIDED>(i, Kh, Vh, N, c0 + kBc, nk, nv, k_src, v_src,
+                                                         wave, kn, vn);
+                };
+
+                // Checking build: the next tile is copied and visible before this
+                // tile's compute starts (its buffers were released at the barrier
+                // that ended the previous tile).
+                if constexpr (kSafeSync) {
+                    if (prefetch) {
+        #pragma unroll
+                        for (int i = 0; i < 2 * kLoads; ++i) load(i);
                     }
-                    pop[2 * kb] = __builtin_convertvector(lo, X8);
-                    pop[2 * kb + 1] = __builtin_convertvector(hi, X8);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
                 }
+                // A wave whose rows all precede this tile has nothing to add.
+                const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
+                if (!active && prefetch && !kSafeSync) {
+        #pragma unroll
+                    for (int i = 0; i < 2 * kLoads; ++i) load(i);
+                }
+                if (active) {
+
+                    // S^T[key][query] = K Q^T for the kBc keys of this tile.
+                    f32x16 s[kBc / 32];
+        #pragma unroll
+                    for (int kb = 0; kb < kBc / 32; ++kb)
+        #pragma unroll
+                        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                    // All K fragments of the tile are requested before the first MFMA,
+                    // so the LDS latency is paid once per tile, not once per k-step.
+                    X8 kf[KS][kBc / 32];
+        #pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+        #pragma unroll
+                        for (int kb = 0; kb < kBc / 32; ++kb)
+                            kf[ks][kb] = *reinterpret_cast<const LDS3 X8 *>(
+                                kt + k_rd[ks] + kb * 32 * D * 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    // The S MFMAs run at raised wave priority: the other wave on this
+                    // SIMD (from another workgroup) then tends to run its softmax while
+                    // this one keeps the matrix core busy, instead of both waves
+                    // alternating instruction by instruction through the same phase.
+                    __builtin_amdgcn_s_setprio(1);
+                    // The next tile's loads go out one per k-step, between the MFMAs.
+        #pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+        #pragma unroll
+                        for (int kb = 0; kb < kBc / 32; ++kb)
+                            s[kb] = Elem<E>::mfma(kf[ks][kb], qop[ks], s[kb]);
+                        if (prefetch && !kSafeSync) {
+        #pragma unroll
+                            for (int i = ks * kTileLoads / KS; i < (ks + 1) * kTileLoads / KS; ++i) load(i);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+
+                    __builtin_amdgcn_s_setprio(0);
+
+                    // All V^T fragments of the tile are requested now; the softmax below
+                    // covers their latency.  Fragment (T, db) is two transpose reads
+                    // (keys 16T+4g+k and 16T+8+4g+k, columns of d-block db).
+                    X8 vf[kBc / 16][D / 32];
+        #pragma unroll
+                    for (int T = 0; T < kBc / 16; ++T)
+        #pragma unroll
+                        for (int db = 0; db < D / 32; ++db) {
+                            const LDS3 char *base = vt + v_rd[db] + T * 16 * D * 2;
+                            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base));
+                            const v4i16 hi =
+                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16 *)(base + 8 * D * 2));
+                            vf[T][db] = __builtin_bit_cast(
+                                X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        }
+
+                    // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
+                    const bool need_mask = (CAUSAL && c0 + kBc - 1 > wrow0) || (c0 + kBc > N);
+                    if (need_mask) {
+                        // visible iff 32kb + 8(r/4) + r%4 <= lim, lim = min(qrow, N-1) - c0 - 4g
+                        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - c0 - 4 * g;
+        #pragma unroll
+                        for (int kb = 0; kb < kBc / 32; ++kb)
+        #pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+                    }
+
+                    // Fast path: probabilities against the current exponent base, with
+                    // no row maximum.  The tile is accepted when every half-row sum is
+                    // at most kSumMax (so every probability is); the test also rejects
+                    // inf / NaN sums, in particular on the first tile, whose base is
+                    // still -inf.  Numerator and denominator share the base, so
+                    // O = acc / l and LSE = base*scale + ln(l) do not depend on where
+                    // the base sits.
+                    X8 pop[kBc / 16];
+                    float rs = 0.f;
+                    auto exps = [&](float mcx) __attribute__((always_inline)) {
+                        rs = 0.f;
+        #pragma unroll
+                        for (int kb = 0; kb < kBc / 32; ++kb) {
+                            f32x8 lo, hi;
+        #pragma unroll
+                            for (int r = 0; r < 8; ++r) {
+                                lo[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, -mcx));
+                                hi[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 8], scale_log2, -mcx));
+                                rs += lo[r];
+                                rs += hi[r];
+                            }
+                            pop[2 * kb] = __builtin_convertvector(lo, X8);
+                            pop[2 * kb + 1] = __builtin_convertvector(hi, X8);
+                        }
+                    };
+                    exps(mc_run);
+                    if (__ballot(!(rs <= kSumMax<E>))) {
+                        // Slow path: the base moves to the row maximum (tile and
+                        // running), the accumulator and sum are rescaled, and the
+                        // tile's probabilities are recomputed against the new base.
+                        float mt = s[0][0];
+        #pragma unroll
+                        for (int kb = 0; kb < kBc / 32; ++kb)
+        #pragma unroll
+                            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+                        {
+                            const auto sw = __builtin_amdgcn_permlane32_swap(
+                                __float_as_uint(mt), __float_as_uint(mt), false, false);
+                            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                        }
+                        const float m_new = fmaxf(m_run, mt);
+                        // A row that has seen no visible key keeps base 0 (its terms are 0).
+                        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                        const float alpha = (m_run == -INFINITY) ? 0.f
+                                                                 : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+                        mc_run = m_use * scale_log2;
+                        m_run = m_use;
+                        l_run *= alpha;
+        #pragma unroll
+                        for (int db = 0; db < D / 32; ++db)
+        #pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                        lr_run *= alpha;
+                        exps(mc_run);
+                    }
+                    l_run += rs;
+
+                    // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15.
+        #pragma unroll
+                    for (int T = 0; T < kBc / 16; ++T)
+        #pragma unroll
+                        for (int db = 0; db < D / 32; ++db)
+                            acc[db] = Elem<E>::mfma(vf[T][db], pop[T], acc[db]);
+                    f32x4 lt = {0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+                    for (int T = 0; T < kBc / 16; ++T) lt = Elem<E>::mfma16(sel, pop[T], lt);
+                    lr_run += lt[0];
+                }
+
+                // The next tile's loads must have landed before anyone reads them, and
+                // every wave must be done with this tile before it is overwritten.
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
             };
-            exps(mc_run);
-            if (__ballot(!(rs <= kSumMax<E>))) {
-                // Slow path: the base moves to the row maximum (tile and
-                // running), the accumulator and sum are rescaled, and the
-                // tile's probabilities are recomputed against the new base.
-                float mt = s[0][0];
-#pragma unroll
-                for (int kb = 0; kb < kBc / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-                {
-                    const auto sw = __builtin_amdgcn_permlane32_swap(
-                        __float_as_uint(mt), __float_as_uint(mt), false, false);
-                    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                }
-                const float m_new = fmaxf(m_run, mt);
-                // A row that has seen no visible key keeps base 0 (its terms are 0).
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = (m_run == -INFINITY) ? 0.f
-                                                         : __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
-                mc_run = m_use * scale_log2;
-                m_run = m_use;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-                lr_run *= alpha;
-                exps(mc_run);
-            }
-            l_run += rs;
 
-            // O^T[d][query] += V^T P^T; k-step T covers keys 16T..16T+15.
-#pragma unroll
-            for (int T = 0; T < kBc / 16; ++T)
-#pragma unroll
+        #pragma unroll
+            for (int i = 0; i < 2 * kLoads; ++i)
+                issue_tile_load<DH, kLoads, STRIDED>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave, kn, vn);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            for (int t = 0; t < n_tiles; t += 2) {
+                step(t, k0, v0, k1, v1);
+                if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
+            }
+
+            // Epilogue: O = acc / (sum of the rounded probabilities), rounded to the
+            // element type; LSE = m*scale + ln(l) with the fp32 sum l.
+            float l_tot;
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                                 __float_as_uint(l_run), false, false);
+                l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            const float inv = 1.f / lr_run;
+            if (qrow < N) {
+                E *orow = O + ooff + (size_t)qrow * on;
+        #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
-                    acc[db] = Elem<E>::mfma(vf[T][db], pop[T], acc[db]);
-            f32x4 lt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int T = 0; T < kBc / 16; ++T) lt = Elem<E>::mfma16(sel, pop[T], lt);
-            lr_run += lt[0];
+        #pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const int col = 32 * db + 8 * a + 4 * g;
+                        if (DH % 32 != 0 && col >= DH) continue;
+                        f32x4 x;
+        #pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
+                        *reinterpret_cast<X4 *>(orow + col) = __builtin_convertvector(x, X4);
+                    }
+                if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
+            }
         }
-
-        // The next tile's loads must have landed before anyone reads them, and
-        // every wave must be done with this tile before it is overwritten.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    };
-
-#pragma unroll
-    for (int i = 0; i < 2 * kLoads; ++i)
-        issue_tile_load<DH, kLoads, STRIDED>(i, Kh, Vh, N, 0, k0, v0, k_src, v_src, wave, kn, vn);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < n_tiles; t += 2) {
-        step(t, k0, v0, k1, v1);
-        if (t + 1 < n_tiles) step(t + 1, k1, v1, k0, v0);
-    }
-
-    // Epilogue: O = acc / (sum of the rounded probabilities), rounded to the
-    // element type; LSE = m*scale + ln(l) with the fp32 sum l.
-    float l_tot;
-    {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
-                                                         __float_as_uint(l_run), false, false);
-        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    const float inv = 1.f / lr_run;
-    if (qrow < N) {
-        E *orow = O + ooff + (size_t)qrow * on;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int col = 32 * db + 8 * a + 4 * g;
-                if (DH % 32 != 0 && col >= DH) continue;
-                f32x4 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * a + e] * inv;
-                *reinterpret_cast<X4 *>(orow + col) = __builtin_convertvector(x, X4);
-            }
-        if (g == 0) LSE[(size_t)bh * N + qrow] = m_run * scale + logf(l_tot);
     }
 }
 
@@ -764,65 +844,12 @@ fwd_pipe_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
     LDS3 char *const vb[kPipeBufs] = {(LDS3 char *)lds_v0, (LDS3 char *)lds_v1,
                                       (LDS3 char *)lds_v2};
 
-    // Static schedule (no atomics, no dispatcher involvement after the
-    // launch): the grid is sized to the workgroup slots of the device and each
-    // workgroup walks its own list of query tiles.  Workgroup w runs on XCD
-    // w mod 8 (workgroups are dealt round-robin over the XCDs).
-    //  * mode 2 (the grid and the heads both divide by 8): XCD x owns heads
-    //    x, x+8, ...; its L = G/8 workgroups take its (head, tile) items in
-    //    rounds of L, head-major with the longest causal tiles first, in snake
-    //    order (round r: workgroup lw takes item rL + lw, or rL + L-1-lw when r
-    //    is odd).  Causal costs fall linearly along a head, so two
-    //    consecutive rounds give every workgroup the same work, and an XCD
-    //    works on about one head at a time, whose K/V its L2 then serves.
-    //  * mode 1 (causal, enough heads to fill the grid): units are the tile
-    //    pairs (nqt-1-i, i) of a head, equal in cost, taken round-robin.
-    //  * mode 0: single tiles round-robin, longest causal tiles first over
-    //    all heads.
-    //  * mode 3: one tile per workgroup, the grid covering every tile, mapped
-    //    by map_block (the dispatcher then balances the workgroups).
-    const int npairs = mode == 1 ? (nqt + 1) / 2 : nqt;
-    const int n_units = n_bh * npairs;
-    const int G = gridDim.x;
-    const int L = G >> 3;
-    const int x = blockIdx.x & 7, lw = blockIdx.x >> 3;
-    const int n_local = (n_bh >> 3) * nqt;
-    const int slot = ((G & 7) == 0) ? x * L + lw : (int)blockIdx.x;
+    // Work items: see sched_item.
     for (int it = 0;; ++it) {
         int bh, qt;
-        if (mode == 3) {
-            if (it > 0) break;
-            map_block(blockIdx.x, G, nqt, CAUSAL, 32 * (8 / W), bh, qt);
-        } else if (mode == 2) {
-            if (it * L >= n_local) break;
-            const int pos = it * L + ((it & 1) ? (L - 1 - lw) : lw);
-            if (pos >= n_local) continue;
-            const int lh = pos / nqt, pq = pos - lh * nqt;
-            bh = lh * 8 + x;
-            qt = CAUSAL ? nqt - 1 - pq : pq;
-        } else if (mode == 1) {
-            const int unit = slot + (it >> 1) * G;
-            if (unit >= n_units) break;
-            bh = unit / npairs;
-            const int pi = unit - bh * npairs;
-            if (it & 1) {
-                if (nqt - 1 - pi == pi) continue;  // the middle tile of an odd count
-                qt = pi;
-            } else {
-                qt = nqt - 1 - pi;
-            }
-        } else {
-            const int unit = slot + it * G;
-            if (unit >= n_units) break;
-            if (CAUSAL) {
-                const int rank = unit / n_bh;
-                bh = unit - rank * n_bh;
-                qt = nqt - 1 - rank;
-            } else {
-                bh = unit / nqt;
-                qt = unit - bh * nqt;
-            }
-        }
+        const int got = sched_item(mode, it, n_bh, nqt, CAUSAL, 32 * (8 / W), bh, qt);
+        if (got == 0) break;
+        if (got == 2) continue;
         {
             // Every wave is done with the previous tile's LDS buffers (and
             // its copies have landed) before this tile's prologue refills them.
@@ -1176,6 +1203,31 @@ int device_cus() {
     return n;
 }
 
+// Schedule of a forward launch with `slots` persistent workgroup slots (see
+// sched_item): mode 2 when the heads and slots split evenly over the XCDs and,
+// under the causal mask, the rounds pair up; tile pairs (mode 1) when there
+// are enough of them to balance; otherwise one workgroup per tile (mode 3).
+void plan_forward(bool causal, int n_bh, int nqt, long slots, int &mode, long &grid) {
+    const long n_tiles = (long)n_bh * nqt;
+    mode = 3;
+    grid = n_tiles;
+    if (n_tiles < slots || slots % 8 != 0) return;
+    if (n_bh % 8 == 0) {
+        const long L = slots / 8, n_local = (long)(n_bh / 8) * nqt;
+        const long rounds = (n_local + L - 1) / L;
+        if (!causal || (n_local % L == 0 && rounds % 2 == 0)) {
+            mode = 2;
+            grid = slots;
+            return;
+        }
+    }
+    const long n_pairs = (long)n_bh * ((nqt + 1) / 2);
+    if (causal && n_pairs >= slots && (n_pairs % slots == 0 || n_pairs >= 4 * slots)) {
+        mode = 1;
+        grid = slots;
+    }
+}
+
 // The launch of fwd_pipe_kernel.  W = 8 (96 KiB of LDS, one workgroup per
 // compute unit): persistent, one workgroup per compute unit, at most one per
 // work unit (modes 0-2).  W = 4: one workgroup per tile (mode 3); the
@@ -1189,20 +1241,9 @@ hipError_t launch_pipe(const void *q, const void *k, const void *v, void *o, flo
     constexpr int kRows = W * kRowsPerWave;
     const int nqt = (N + kRows - 1) / kRows;
     const int n_bh = B * H;
-    const long n_tiles = (long)n_bh * nqt;
     int mode = 3;
-    long grid = n_tiles;
-    if (W == 8) {
-        const long slots = device_cus();
-        const long n_pairs = (long)n_bh * ((nqt + 1) / 2);
-        mode = 0;
-        if (n_tiles >= slots && slots % 8 == 0 && n_bh % 8 == 0)
-            mode = 2;
-        else if (CAUSAL && n_pairs >= slots)
-            mode = 1;
-        const long n_units = mode == 1 ? n_pairs : n_tiles;
-        grid = n_units < slots ? n_units : slots;
-    }
+    long grid = (long)n_bh * nqt;
+    if (W == 8) plan_forward(CAUSAL, n_bh, nqt, device_cus(), mode, grid);
     hipLaunchKernelGGL((fwd_pipe_kernel<E, D, CAUSAL, STRIDED, W>), dim3((int)grid), dim3(64 * W),
                        0, stream, static_cast<const E *>(q), static_cast<const E *>(k),
                        static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, n_bh, mode,
@@ -1224,11 +1265,18 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
                                                                         scale, scale_log2, st,
                                                                         stream);
         }
+        // One workgroup per tile (mode 3).  The persistent schedules
+        // (two workgroups per compute unit) measured slower here, same box:
+        // B16 H12 N1000 d64 651 vs 700 TFLOP/s non-causal, 502 vs 529 causal,
+        // B4 H16 N2048 d64 level; with rows this short a workgroup's
+        // prologue (Q load, first tiles) is a large share of its time, and
+        // other workgroups on the unit cover it only under the dispatcher.
         const int nqt = (N + kBr - 1) / kBr;
-        hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(B * H * nqt), dim3(kThreads),
+        const int n_bh = B * H;
+        hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(n_bh * nqt), dim3(kThreads),
                            0, stream, static_cast<const E *>(q), static_cast<const E *>(k),
-                           static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, scale,
-                           scale_log2, st);
+                           static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, n_bh, 3,
+                           scale, scale_log2, st);
     }
     return hipGetLastError();
 }
