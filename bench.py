@@ -40,8 +40,10 @@ thread, and prints the host's CPU model.
 Counter helpers (used to produce the summaries under profiles/):
   python bench.py --copy-calibration ...   also runs one plain device copy
                                            of 1 GiB (for counter scaling)
-  python bench.py --summarize-trace DIR CMD       per-kernel summary of a
+  python bench.py --summarize-trace DIR CMD [K [FLOPS [PEAK]]]
+                                                  per-kernel summary of a
                                                   --kernel-trace --stats run
+                                                  (mean of the last K dispatches)
   python bench.py --summarize-counters FDIR WDIR WORKLOAD CMD [KERNEL]
                                                   traffic summary of the
                                                   FETCH_SIZE / WRITE_SIZE runs
@@ -244,22 +246,39 @@ def _db_rows(directory: str, query: str):
     return rows
 
 
-def summarize_trace(directory: str, command: str) -> None:
+def summarize_trace(directory: str, command: str, timed: int = 0, flops: float = 0.0,
+                    peak: float = PEAK_BF16_TFLOPS) -> None:
     """Print the per-kernel summary of a `rocprofv3 --kernel-trace --stats`
-    run (SQLite output under `directory`)."""
+    run (SQLite output under `directory`).  With `timed` > 0, also the mean
+    duration of the last `timed` dispatches of the most frequent kernel (the
+    timed steps of the traced bench command, after its warm-up launches) and,
+    with `flops`, the TFLOP/s and fraction of the bf16 peak it gives."""
     print(f"COMMAND: {command}")
     print("KERNEL_SOURCE_SHA256_16:", kernel_source_hash())
     print("BWD_KERNEL_SOURCE_SHA256_16:", kernel_source_hash(BWD_KERNEL_SOURCES))
     print("kernel | calls | total_ms | average_us | percent")
-    for name, calls, total, avg, pct in _db_rows(
-            directory, "select name, total_calls, total_duration, average, percentage "
-                       "from top_kernels"):
+    top = _db_rows(directory, "select name, total_calls, total_duration, average, percentage "
+                              "from top_kernels")
+    for name, calls, total, avg, pct in top:
         # rocprofv3 reports these two columns in microseconds
         print(f"{name} | {calls} | {total / 1e3:.3f} | {avg:.2f} | {pct:.1f}")
     for name, vgpr, agpr, sgpr, lds, scratch in _db_rows(
             directory, "select distinct name, vgpr_count, accum_vgpr_count, sgpr_count, "
                        "lds_size, scratch_size from kernels"):
         print(f"resources {name}: vgpr={vgpr} agpr={agpr} sgpr={sgpr} lds={lds} scratch={scratch}")
+    if timed and top:
+        name = max(top, key=lambda r: r[1])[0]
+        durs = [d for n, d in _db_rows(directory, "select name, duration from kernels "
+                                                  "order by start") if n == name]
+        last = durs[-timed:]
+        us = sum(last) / len(last) / 1e3
+        print("DISPATCH_US (in order): " + ", ".join(f"{d / 1e3:.1f}" for d in durs))
+        print(f"TIMED_DISPATCHES: last {len(last)} of {len(durs)}")
+        print(f"TIMED_MEAN_US: {us:.2f}")
+        if flops:
+            tf = flops / (us * 1e-6) / 1e12
+            print(f"TIMED_TFLOPS: {tf:.3f}")
+            print(f"TIMED_FRACTION_OF_PEAK ({peak} TFLOP/s): {tf / peak:.4f}")
 
 
 def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str,
@@ -415,18 +434,30 @@ def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
     under `dirs` for the kernels whose name contains `kernel`, and derived
     figures.  GRBM_GUI_ACTIVE is the sum over the 8 XCDs of each XCD's active
     cycles; SQ_VALU_MFMA_BUSY_CYCLES the sum over the 1024 SIMDs of their
-    matrix-core busy cycles (32 per 32x32x16 MFMA).  Hence the shader clock
-    = GRBM_GUI_ACTIVE / 8 / mean duration (from the kernel trace in
-    `trace_dir`), the MFMA-busy fraction = SQ_VALU_MFMA_BUSY_CYCLES /
-    (1024 * GRBM_GUI_ACTIVE / 8), and the same busy cycles against 2.4 GHz;
-    the VALU issue fraction = 4 * SQ_ACTIVE_INST_VALU (quad-cycles, MFMA issue
-    included) / (1024 * GRBM_GUI_ACTIVE / 8)."""
-    vals = {}
+    matrix-core busy cycles (32 per 32x32x16 MFMA, 16 per 16x16x32).  Each
+    counter record carries its dispatch's start and end, so the shader clock
+    of a dispatch is GRBM_GUI_ACTIVE / 8 / its duration; the MFMA-busy
+    fraction is SQ_VALU_MFMA_BUSY_CYCLES / (1024 * GRBM_GUI_ACTIVE / 8) of the
+    kernel's cycles (and, times the clock / 2.4 GHz, of the nominal peak); the
+    VALU issue fraction = 4 * SQ_ACTIVE_INST_VALU (quad-cycles, MFMA issue
+    included) / (1024 * GRBM_GUI_ACTIVE / 8).  `trace_dir` (a kernel trace of
+    the same command) is reported beside them."""
+    vals, clocks, busy = {}, [], []
+    per_dispatch = {}
     for d in dirs:
-        for name, counter, value in _db_rows(
-                d, "select kernel_name, counter_name, value from counters_collection"):
+        for name, counter, value, start, end, disp in _db_rows(
+                d, "select kernel_name, counter_name, value, start, end, dispatch_id "
+                   "from counters_collection"):
             if kernel in name:
                 vals.setdefault(counter, []).append(value)
+                per_dispatch.setdefault((d, disp), {})[counter] = (value, start, end)
+    for rec in per_dispatch.values():
+        if "GRBM_GUI_ACTIVE" in rec:
+            v, start, end = rec["GRBM_GUI_ACTIVE"]
+            if end > start:
+                clocks.append(v / 8.0 / (end - start))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in rec:
+                busy.append(rec["SQ_VALU_MFMA_BUSY_CYCLES"][0] / (1024.0 * v / 8.0))
     durs = [avg for name, _, _, avg, _ in _db_rows(
         trace_dir, "select name, total_calls, total_duration, average, percentage from top_kernels")
         if kernel in name]
@@ -438,19 +469,30 @@ def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
         mean[c] = sum(vals[c]) / len(vals[c])
         print(f"{c} | {len(vals[c])} | {mean[c]:.6g}")
     xcd_cycles = mean.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+    if xcd_cycles:
+        print(f"CYCLES_PER_DISPATCH_PER_XCD: {xcd_cycles:.4g}")
+    if clocks:
+        print("SHADER_CLOCK_GHZ_PER_DISPATCH: " + ", ".join(f"{c:.3f}" for c in clocks))
+        print(f"SHADER_CLOCK_GHZ: {sum(clocks) / len(clocks):.3f}")
+    if busy:
+        b = sum(busy) / len(busy)
+        print(f"MFMA_BUSY_FRACTION: {b:.3f}")
+        if clocks:
+            print(f"MFMA_BUSY_FRACTION_AT_2.4GHZ: {b * (sum(clocks) / len(clocks)) / 2.4:.3f}")
     if durs:
-        us = durs[0]
-        print(f"MEAN_DURATION_US (kernel trace): {us:.2f}")
-        if xcd_cycles:
-            print(f"SHADER_CLOCK_GHZ: {xcd_cycles / (us * 1e3):.3f}")
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-            print(f"MFMA_BUSY_FRACTION_AT_2.4GHZ: "
-                  f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * us * 1e-6 * 2.4e9):.3f}")
-    if xcd_cycles and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-        print(f"MFMA_BUSY_FRACTION: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * xcd_cycles):.3f}")
+        print(f"MEAN_DURATION_US (kernel trace, every dispatch): {durs[0]:.2f}")
     if xcd_cycles and "SQ_ACTIVE_INST_VALU" in mean:
         # SQ_ACTIVE_INST_VALU counts issue quad-cycles (4 clocks) summed over waves
         print(f"VALU_ISSUE_FRACTION: {4 * mean['SQ_ACTIVE_INST_VALU'] / (1024 * xcd_cycles):.3f}")
+    if xcd_cycles and "SQ_INSTS_MFMA" in mean:
+        per_simd = {c: mean[c] / 1024 for c in mean if c.startswith("SQ_INSTS")}
+        print("INSTRUCTIONS_PER_SIMD_PER_DISPATCH: " +
+              ", ".join(f"{c[9:]}={v:.4g}" for c, v in sorted(per_simd.items())))
+        m = mean["SQ_INSTS_MFMA"]
+        if m:
+            print("PER_MFMA: " + ", ".join(f"{c[9:]}={mean[c] / m:.2f}"
+                                          for c in sorted(mean) if c.startswith("SQ_INSTS")
+                                          and c != "SQ_INSTS_MFMA"))
     if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_ACTIVE_INST_LDS" in mean and mean["SQ_ACTIVE_INST_LDS"]:
         print(f"LDS_BANK_CONFLICT_PER_LDS_ACTIVE_CYCLE: "
               f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_ACTIVE_INST_LDS']:.4f}")
@@ -472,7 +514,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "COMMAND"))
+    ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                    help="DIR COMMAND [TIMED_STEPS [FLOPS]]")
     ap.add_argument("--summarize-counters", nargs="+",
                     metavar="ARG", help="FETCH_DIR WRITE_DIR WORKLOAD COMMAND [KERNEL_SUBSTRING]")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG")
@@ -489,7 +532,10 @@ def main() -> int:
         return 0
 
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace)
+        a = args.summarize_trace
+        summarize_trace(a[0], a[1], int(a[2]) if len(a) > 2 else 0,
+                        float(a[3]) if len(a) > 3 else 0.0,
+                        float(a[4]) if len(a) > 4 else PEAK_BF16_TFLOPS)
         return 0
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters[:5])
