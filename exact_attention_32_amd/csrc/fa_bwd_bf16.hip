@@ -64,8 +64,6 @@ template <int D>
 constexpr int kDqWaves = 2;
 template <int D>
 constexpr int kDkdvWaves = 2;
-template <int D>
-constexpr int kHalfUnroll = D == 128 ? 1 : 2;
 
 // Element strides (batch, head, row) of the eight [B, H, N, d] tensors, d
 // contiguous, in the order of the enum below; LSE and delta stay dense
@@ -193,37 +191,35 @@ bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restr
         }
         const bool active = !CAUSAL || c0 <= wrow0 + kRowsPerWave - 1;
         if (active) {
-            // S^T = K Q^T and dP^T = V dO^T (keys x queries).
-            f32x16 s[kInner / 32], dp[kInner / 32];
-#pragma unroll
-            for (int kb = 0; kb < kInner / 32; ++kb)
+            // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
+            const bool need_mask = (CAUSAL && c0 + kInner - 1 > wrow0) || (c0 + kInner > N);
+            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - c0 - 4 * g;
+            f32x16 s[2], dp[2];
+            X8 dsop[4];
+            // S^T = K Q^T and dP^T = V dO^T for the 32 keys of block kb.
+            auto products = [&](int kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < kInner / 32; ++kb) {
+                for (int ks = 0; ks < KS; ++ks) {
                     const uint32_t a = row_read_at(rd, ks) + kb * 32 * D * 2;
                     const X8 kf = *reinterpret_cast<const LDS3 X8 *>(kt + a);
                     const X8 vf = *reinterpret_cast<const LDS3 X8 *>(vt + a);
                     s[kb] = TileOps<E>::mfma(kf, qop[ks], s[kb]);
                     dp[kb] = TileOps<E>::mfma(vf, doop[ks], dp[kb]);
                 }
-            // Element r of s[kb] is key c0 + 32kb + 8(r/4) + 4g + r%4.
-            const bool need_mask = (CAUSAL && c0 + kInner - 1 > wrow0) || (c0 + kInner > N);
-            if (need_mask) {
-                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - c0 - 4 * g;
-#pragma unroll
-                for (int kb = 0; kb < kInner / 32; ++kb)
+            };
+            auto mask = [&](int kb) {
+                if (need_mask) {
+                    keep_branch();
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
-            }
-            // dS^T = P^T o (dP^T - D), rounded to bf16 as the B operand of
-            // the next product (rows 0-7 / 8-15 of a block are two k-steps).
-            X8 dsop[kInner / 16];
-#pragma unroll
-            for (int kb = 0; kb < kInner / 32; ++kb) {
+                }
+            };
+            // dS^T = P^T o (dP^T - D) of block kb, rounded to bf16 as the B
+            // operands of k-steps 2kb (rows 0-7) and 2kb + 1 (rows 8-15).
+            auto dscores = [&](int kb) {
                 f32x8 lo, hi;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
@@ -234,13 +230,44 @@ bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restr
                 }
                 dsop[2 * kb] = __builtin_convertvector(lo, X8);
                 dsop[2 * kb + 1] = __builtin_convertvector(hi, X8);
-            }
-            // dQ^T += K^T dS^T; k-step T covers keys 16T .. 16T+15.
-#pragma unroll
-            for (int T = 0; T < kInner / 16; ++T)
+            };
+            // dQ^T += K^T dS^T over k-steps T (keys 16T .. 16T + 15).
+            auto dq_products = [&](int T) {
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
                     acc[db] = TileOps<E>::mfma(tr_read<D, X8>(kt, trd, T, db), dsop[T], acc[db]);
+            };
+            // Block 1's products run on the matrix core while the vector
+            // unit forms block 0's dS; block 0's dQ products while it forms
+            // block 1's.
+            products(0);
+            mask(0);
+            products(1);
+            dscores(0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                if (i < 2 * KS - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            pin(dsop[0]);  // formed here, not moved past the mask branch
+            pin(dsop[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mask(1);
+            dq_products(0);
+            dq_products(1);
+            dscores(1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * D / 32; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+                if (i < 2 * D / 32 - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            dq_products(2);
+            dq_products(3);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -348,7 +375,8 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
     auto load_all = [&](int c0, LDS3 char *dq_, LDS3 char *do_, LDS3 float *st) {
         load_tile<D, DH, STRIDED>(Qh, N, c0, dq_, qsrc, wave, qn);
         load_tile<D, DH, STRIDED>(dOh, N, c0, do_, dosrc, wave, don);
-        if (wave < 2) load_vec(wave == 0 ? LSEh : Dh, N, c0, st + wave * kInner, lane);
+        if (wave < 2)
+            load_vec(wave == 0 ? LSEh : Dh, N, c0, st + wave * kInner, opaque(lane));
     };
 
     auto step = [&](int t, const LDS3 char *qt_, const LDS3 char *ot_, const LDS3 float *st,
@@ -364,9 +392,10 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
         if (active) {
             // Two halves of 32 queries; element r of a half's block is query
             // c0 + 32qb + 8(r/4) + 4g + r%4 (and the lane's key).
-#pragma unroll kHalfUnroll<D>
-            for (int qb = 0; qb < kInner / 32; ++qb) {
-                f32x16 s = {}, dp = {};
+            // S = Q K^T and dP = dO V^T of half qb.
+            auto products = [&](int qb, f32x16 &s, f32x16 &dp) {
+                s = f32x16{};
+                dp = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const uint32_t a = row_read_at(rd, ks) + qb * 32 * D * 2;
@@ -375,9 +404,11 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
                     s = TileOps<E>::mfma(qf, kop[ks], s);
                     dp = TileOps<E>::mfma(of, vop[ks], dp);
                 }
+            };
+            auto mask = [&](int qb, f32x16 &s) {
                 const int qbase = c0 + 32 * qb;
-                const bool need_mask = (CAUSAL && qbase < wk0 + kRowsPerWave - 1) || (qbase + 32 > N);
-                if (need_mask) {
+                if ((CAUSAL && qbase < wk0 + kRowsPerWave - 1) || (qbase + 32 > N)) {
+                    keep_branch();
                     // visible iff query >= key (causal) and query < N
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -385,6 +416,10 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
                         if (qi >= N || (CAUSAL && qi < key)) s[r] = -INFINITY;
                     }
                 }
+            };
+            // P and dS = P o (dP - D), rounded to the element type as the B
+            // operands of k-steps 2qb (queries 0-15 of the half) and 2qb + 1.
+            auto scores = [&](int qb, const f32x16 &s, const f32x16 &dp, X8 *pop, X8 *dsop) {
                 f32x8 plo, phi, dlo, dhi;
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
@@ -399,10 +434,13 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
                         else { phi[r - 8] = p; dhi[r - 8] = ds; }
                     }
                 }
-                const X8 pop[2] = {__builtin_convertvector(plo, X8), __builtin_convertvector(phi, X8)};
-                const X8 dsop[2] = {__builtin_convertvector(dlo, X8), __builtin_convertvector(dhi, X8)};
-                // dV^T += dO^T P and dK^T += Q^T dS over the half's 32 queries
-                // (k-steps T = 2qb, 2qb + 1).
+                pop[0] = __builtin_convertvector(plo, X8);
+                pop[1] = __builtin_convertvector(phi, X8);
+                dsop[0] = __builtin_convertvector(dlo, X8);
+                dsop[1] = __builtin_convertvector(dhi, X8);
+            };
+            // dV^T += dO^T P and dK^T += Q^T dS over the half's 32 queries.
+            auto key_products = [&](int qb, const X8 *pop, const X8 *dsop) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -412,6 +450,78 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
                         acck[db] = TileOps<E>::mfma(tr_read<D, X8>(qt_, trd, 2 * qb + h, db), dsop[h],
                                                     acck[db]);
                     }
+            };
+            if constexpr (D == 64) {
+                // Registers allow the halves to overlap: half 1's S and dP
+                // run on the matrix core while the vector unit forms half 0's
+                // P and dS, and half 0's dV and dK products while it forms
+                // half 1's.
+                constexpr int kScoreValu = 88;  // per half: 16 x (exp, 2 fma/mul, sub, mul) + 8 cvt
+                f32x16 s0, dp0, s1, dp1;
+                X8 pop0[2], dsop0[2], pop1[2], dsop1[2];
+                products(0, s0, dp0);
+                mask(0, s0);
+                products(1, s1, dp1);
+                scores(0, s0, dp0, pop0, dsop0);
+#pragma unroll
+                for (int i = 0; i < 2 * KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kScoreValu / (2 * KS), 0);
+                }
+                pin(pop0[0]);  // formed here, not moved past the mask branch
+                pin(pop0[1]);
+                pin(dsop0[0]);
+                pin(dsop0[1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mask(1, s1);
+                key_products(0, pop0, dsop0);
+                scores(1, s1, dp1, pop1, dsop1);
+#pragma unroll
+                for (int i = 0; i < 4 * D / 32; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kScoreValu / (4 * D / 32), 0);
+                }
+                pin(pop1[0]);
+                pin(pop1[1]);
+                pin(dsop1[0]);
+                pin(dsop1[1]);
+                __builtin_amdgcn_sched_barrier(0);
+                key_products(1, pop1, dsop1);
+            } else {
+                // K, V and both accumulators take 192 registers at d = 128:
+                // one half at a time, as a loop (not unrolled), which keeps
+                // the halves' live ranges apart.
+#pragma unroll 1
+                for (int qb = 0; qb < kInner / 32; ++qb) {
+                    f32x16 s = {}, dp = {};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const uint32_t a = row_read_at(rd, ks) + qb * 32 * D * 2;
+                        const X8 qf = *reinterpret_cast<const LDS3 X8 *>(qt_ + a);
+                        s = TileOps<E>::mfma(qf, kop[ks], s);
+                        const X8 of = *reinterpret_cast<const LDS3 X8 *>(ot_ + a);
+                        dp = TileOps<E>::mfma(of, vop[ks], dp);
+                    }
+                    mask(qb, s);
+                    f32x8 plo, phi, dlo, dhi;
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const f32x4 l4 = *reinterpret_cast<const LDS3 f32x4 *>(st + 32 * qb + 8 * a + 4 * g);
+                        const f32x4 d4 =
+                            *reinterpret_cast<const LDS3 f32x4 *>(st + kInner + 32 * qb + 8 * a + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * a + e;
+                            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -l4[e] * kLog2e));
+                            const float ds = p * (dp[r] - d4[e]);
+                            if (r < 8) { plo[r] = p; dlo[r] = ds; }
+                            else { phi[r - 8] = p; dhi[r - 8] = ds; }
+                        }
+                    }
+                    const X8 pop[2] = {__builtin_convertvector(plo, X8), __builtin_convertvector(phi, X8)};
+                    const X8 dsop[2] = {__builtin_convertvector(dlo, X8), __builtin_convertvector(dhi, X8)};
+                    key_products(qb, pop, dsop);
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -430,11 +540,12 @@ bwd_dkdv_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__res
         }
     }
     if (valid) {
+        const int skey = opaque(key);
         store_rows<D, DH>(dK + head_offset<DH, STRIDED>(st, bh, N, kTDK) +
-                              (size_t)key * row_stride<DH, STRIDED>(st, kTDK),
+                              (size_t)skey * row_stride<DH, STRIDED>(st, kTDK),
                           acck, scale, g);
         store_rows<D, DH>(dV + head_offset<DH, STRIDED>(st, bh, N, kTDV) +
-                              (size_t)key * row_stride<DH, STRIDED>(st, kTDV),
+                              (size_t)skey * row_stride<DH, STRIDED>(st, kTDV),
                           accv, 1.f, g);
     }
 }

@@ -32,6 +32,26 @@ constexpr int kOuter = kWaves * kRowsPerWave;  // rows owned by one workgroup
 constexpr int kInner = 64;                  // rows per streamed tile
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Placed first in a block that runs under a uniform condition (a tile's
+// element mask): an empty statement with side effects, so the optimiser
+// cannot turn the block into selects that every tile would then execute.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+
+// The same value, unknown to the optimiser at this point: what is derived
+// from it is computed here, not hoisted and kept in registers from an
+// earlier use (loop-invariant lane offsets under register pressure).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Marks a value as used at this point, so that the optimiser computes it
+// before here (in this block) rather than next to its later use.
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+    asm volatile("" : "+v"(x));
+}
+
 // Operand vectors and the 32x32x16 MFMA (fp32 accumulation) of an element
 // type.
 template <typename E>
@@ -137,8 +157,10 @@ __device__ __forceinline__ void load_tile(const void *mat, int N, int r0, LDS3 c
     constexpr int kRowsPerLoad = kWaves * 1024 / (D * 2);
     const int stride = STRIDED ? rs : DH;
     const uint32_t rows = (uint32_t)max(0, min(kInner, N - r0));
-    const uint32_t bytes = STRIDED ? (rows ? (rows - 1) * (uint32_t)rs * 2u + DH * 2u : 0u)
-                                   : rows * (uint32_t)(DH * 2);
+    // (readfirstlane: the clamp compiles to a vector med3, and a descriptor
+    // in vector registers would be wrapped in a per-lane waterfall loop)
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane(
+        STRIDED ? (rows ? (rows - 1) * (uint32_t)rs * 2u + DH * 2u : 0u) : rows * (uint32_t)(DH * 2));
     const __amdgpu_buffer_rsrc_t rsrc =
         make_rsrc((const char *)mat + (size_t)r0 * (size_t)stride * 2, bytes);
 #pragma unroll
@@ -152,7 +174,7 @@ __device__ __forceinline__ void load_tile(const void *mat, int N, int r0, LDS3 c
 // as 0) into dst[0 .. 63], one 4-byte load per lane of the calling wave.
 __device__ __forceinline__ void load_vec(const float *vec, int N, int c0, LDS3 float *dst,
                                          int lane) {
-    const uint32_t bytes = (uint32_t)max(0, min(kInner, N - c0)) * 4u;
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(kInner, N - c0)) * 4u);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(vec + c0, bytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS3 void *)dst, 4, (uint32_t)lane * 4u, 0, 0, 0);
 }
