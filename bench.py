@@ -129,16 +129,16 @@ ORACLE_TIMING_WORKLOADS = ["w1_f32_n256_d64", "w2_bf16_b4h16_n2048_d64",
                            "w5a_bf16_b16h12_n1000_d64", "w5b_bf16_b16h12_n1000_d64_causal"]
 
 
-def oracle_timing_child(name: str) -> None:
+def oracle_timing_child(name: str, threads: int) -> None:
     """Time the oracle's full forward pass (every row, the plain definition)
-    on one workload with the OpenMP thread count this process was started
-    with; print one JSON line."""
+    on one workload with `threads` OpenMP threads; print one JSON line."""
     import oracle
     from exact_attention_32_amd import inputs
 
     w = inputs.WORKLOADS[name]
     q, k, v = inputs.make_qkv(w)
     o = oracle.default()
+    o.set_num_threads(threads)
     o.attention(q[:, :1, :8], k[:, :1, :8], v[:, :1, :8], w.scale, w.causal)  # warm-up
     t0 = time.perf_counter()
     o.attention(q, k, v, w.scale, w.causal)
@@ -154,16 +154,20 @@ def oracle_timings() -> int:
     import subprocess
 
     rows = []
+    # every thread this job may use: OMP_NUM_THREADS where the host sets a
+    # share, else every host thread
+    share = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count() or 1)
     for name in ORACLE_TIMING_WORKLOADS:
-        for threads in ("1", str(os.cpu_count() or 1)):
+        for threads in ("1", share):
             env = dict(os.environ, OMP_NUM_THREADS=threads)
             r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-timing-child",
-                                name], env=env, capture_output=True, text=True, check=True)
+                                name, "--oracle-threads", threads], env=env,
+                               capture_output=True, text=True, check=True)
             line = json.loads(r.stdout.strip().splitlines()[-1])
             print(json.dumps(line), flush=True)
             rows.append(line)
     print(json.dumps({"oracle_timings": rows, "cpu_model": cpu_model(),
-                      "host_threads": os.cpu_count()}), flush=True)
+                      "host_threads": os.cpu_count(), "threads_used": int(share)}), flush=True)
     return 0
 
 
@@ -523,12 +527,13 @@ def main() -> int:
                     help="time the oracle on the small workloads on one core and on all "
                          "host threads (no GPU)")
     ap.add_argument("--oracle-timing-child", metavar="WORKLOAD", help=argparse.SUPPRESS)
+    ap.add_argument("--oracle-threads", type=int, default=1, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.oracle_timings:
         return oracle_timings()
     if args.oracle_timing_child:
-        oracle_timing_child(args.oracle_timing_child)
+        oracle_timing_child(args.oracle_timing_child, args.oracle_threads)
         return 0
 
     if args.summarize_trace:

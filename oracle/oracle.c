@@ -410,6 +410,16 @@ int oracle_attention_backward_kv_keys(const double *q, const double *k, const do
     return 0;
 }
 
+/* Sets the number of OpenMP threads of later parallel regions (n >= 1). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_num_threads(void)
 {

@@ -91,6 +91,8 @@ class Oracle:
             ctypes.c_double, ctypes.c_int, _D, _D]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self._lib = lib
 
     # -- safe softmax of one vector (eq. (2)-(5)) --------------------------
@@ -216,6 +218,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self._lib.oracle_set_num_threads(int(n))
 
 
 def default() -> Oracle:
