@@ -364,8 +364,10 @@ struct FwdStrides {
     int qn, kn, vn, on, H;
 };
 
-template <typename E, int DH, bool CAUSAL, bool STRIDED>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// OCC: waves per SIMD the kernel is compiled for (2, or 3 at d = 64: 168
+// registers instead of 176, three workgroups per compute unit).
+template <typename E, int DH, bool CAUSAL, bool STRIDED, int OCC = 2>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
            E *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int n_bh, int mode,
            float scale, float scale_log2, FwdStrides st) {
@@ -1228,6 +1230,15 @@ void plan_forward(bool causal, int n_bh, int nqt, long slots, int &mode, long &g
     }
 }
 
+// True when `tiles` workgroups fill the slots of three workgroups per
+// compute unit at least as evenly as those of two (the last round's share
+// of occupied slots).
+bool fills_as_evenly(long tiles, int cus) {
+    const long s2 = 2L * cus, s3 = 3L * cus;
+    const long r2 = (tiles + s2 - 1) / s2, r3 = (tiles + s3 - 1) / s3;
+    return r3 * s3 <= r2 * s2;
+}
+
 // The launch of fwd_pipe_kernel.  W = 8 (96 KiB of LDS, one workgroup per
 // compute unit): persistent, one workgroup per compute unit, at most one per
 // work unit (modes 0-2).  W = 4: one workgroup per tile (mode 3); the
@@ -1273,6 +1284,21 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
         // other workgroups on the unit cover it only under the dispatcher.
         const int nqt = (N + kBr - 1) / kBr;
         const int n_bh = B * H;
+        if constexpr (D == 64) {
+            // Three workgroups per compute unit (a few registers go to
+            // scratch) when the grid fills three slots per unit as evenly as
+            // two, or under the causal mask, where the largest-first order
+            // balances uneven workgroups: B16 H12 N1000 d64 +4 % causal, +5 %
+            // non-causal; B4 H16 N2048 d64 (two full rounds of two, 1.33 of
+            // three) 3 % slower, so it keeps two.
+            if (CAUSAL || fills_as_evenly((long)n_bh * nqt, device_cus())) {
+                hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED, 3>), dim3(n_bh * nqt),
+                                   dim3(kThreads), 0, stream, static_cast<const E *>(q),
+                                   static_cast<const E *>(k), static_cast<const E *>(v),
+                                   static_cast<E *>(o), lse, N, nqt, n_bh, 3, scale, scale_log2, st);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, STRIDED>), dim3(n_bh * nqt), dim3(kThreads),
                            0, stream, static_cast<const E *>(q), static_cast<const E *>(k),
                            static_cast<const E *>(v), static_cast<E *>(o), lse, N, nqt, n_bh, 3,
