@@ -436,17 +436,22 @@ def bench_decode(args) -> int:
 def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
     """Per-dispatch averages of the counters collected in the `--pmc` runs
     under `dirs` for the kernels whose name contains `kernel`, and derived
-    figures.  GRBM_GUI_ACTIVE is the sum over the 8 XCDs of each XCD's active
-    cycles; SQ_VALU_MFMA_BUSY_CYCLES the sum over the 1024 SIMDs of their
-    matrix-core busy cycles (32 per 32x32x16 MFMA, 16 per 16x16x32).  Each
-    counter record carries its dispatch's start and end, so the shader clock
-    of a dispatch is GRBM_GUI_ACTIVE / 8 / its duration; the MFMA-busy
-    fraction is SQ_VALU_MFMA_BUSY_CYCLES / (1024 * GRBM_GUI_ACTIVE / 8) of the
-    kernel's cycles (and, times the clock / 2.4 GHz, of the nominal peak); the
-    VALU issue fraction = 4 * SQ_ACTIVE_INST_VALU (quad-cycles, MFMA issue
-    included) / (1024 * GRBM_GUI_ACTIVE / 8).  `trace_dir` (a kernel trace of
-    the same command) is reported beside them."""
-    vals, clocks, busy = {}, [], []
+    figures.  SQ_BUSY_CYCLES is the sum over the 32 shader engines (8 XCDs x
+    4) of their busy cycles; SQ_VALU_MFMA_BUSY_CYCLES the sum over the 1024
+    SIMDs of their matrix-core busy cycles (32 per 32x32x16 MFMA, 16 per
+    16x16x32).  Each counter record carries its dispatch's start and end, so
+    the shader clock of a dispatch is SQ_BUSY_CYCLES / 32 / its duration; the
+    MFMA-busy fraction is SQ_VALU_MFMA_BUSY_CYCLES / (1024 * SQ_BUSY_CYCLES /
+    32) of the kernel's cycles, and SQ_VALU_MFMA_BUSY_CYCLES / (1024 *
+    duration * 2.4 GHz) of the nominal peak; the VALU issue fraction = 4 *
+    SQ_ACTIVE_INST_VALU (quad-cycles, MFMA issue included) / (1024 *
+    SQ_BUSY_CYCLES / 32).  (GRBM_GUI_ACTIVE / 8 counts each XCD's cycles over
+    the whole counter window around the dispatch: close to the shader
+    engines' busy cycles for millisecond kernels, up to twice them for
+    kernels of tens of microseconds; it is printed but not used.)
+    `trace_dir` (a kernel trace of the same command) is reported beside
+    them."""
+    vals, clocks, busy, peak_frac = {}, [], [], []
     per_dispatch = {}
     for d in dirs:
         for name, counter, value, start, end, disp in _db_rows(
@@ -456,12 +461,15 @@ def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
                 vals.setdefault(counter, []).append(value)
                 per_dispatch.setdefault((d, disp), {})[counter] = (value, start, end)
     for rec in per_dispatch.values():
-        if "GRBM_GUI_ACTIVE" in rec:
-            v, start, end = rec["GRBM_GUI_ACTIVE"]
+        if "SQ_BUSY_CYCLES" in rec:
+            v, start, end = rec["SQ_BUSY_CYCLES"]
             if end > start:
-                clocks.append(v / 8.0 / (end - start))
+                clocks.append(v / 32.0 / (end - start))
             if "SQ_VALU_MFMA_BUSY_CYCLES" in rec:
-                busy.append(rec["SQ_VALU_MFMA_BUSY_CYCLES"][0] / (1024.0 * v / 8.0))
+                m = rec["SQ_VALU_MFMA_BUSY_CYCLES"][0]
+                busy.append(m / (1024.0 * v / 32.0))
+                if end > start:
+                    peak_frac.append(m / 1024.0 / ((end - start) * 2.4))
     durs = [avg for name, _, _, avg, _ in _db_rows(
         trace_dir, "select name, total_calls, total_duration, average, percentage from top_kernels")
         if kernel in name]
@@ -472,23 +480,22 @@ def summarize_pmc(kernel: str, trace_dir: str, command: str, dirs) -> None:
     for c in sorted(vals):
         mean[c] = sum(vals[c]) / len(vals[c])
         print(f"{c} | {len(vals[c])} | {mean[c]:.6g}")
-    xcd_cycles = mean.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
-    if xcd_cycles:
-        print(f"CYCLES_PER_DISPATCH_PER_XCD: {xcd_cycles:.4g}")
+    se_cycles = mean.get("SQ_BUSY_CYCLES", 0.0) / 32.0
+    if se_cycles:
+        print(f"BUSY_CYCLES_PER_DISPATCH_PER_SHADER_ENGINE: {se_cycles:.4g}")
     if clocks:
         print("SHADER_CLOCK_GHZ_PER_DISPATCH: " + ", ".join(f"{c:.3f}" for c in clocks))
         print(f"SHADER_CLOCK_GHZ: {sum(clocks) / len(clocks):.3f}")
     if busy:
-        b = sum(busy) / len(busy)
-        print(f"MFMA_BUSY_FRACTION: {b:.3f}")
-        if clocks:
-            print(f"MFMA_BUSY_FRACTION_AT_2.4GHZ: {b * (sum(clocks) / len(clocks)) / 2.4:.3f}")
+        print(f"MFMA_BUSY_FRACTION: {sum(busy) / len(busy):.3f}")
+    if peak_frac:
+        print(f"MFMA_BUSY_FRACTION_AT_2.4GHZ: {sum(peak_frac) / len(peak_frac):.3f}")
     if durs:
         print(f"MEAN_DURATION_US (kernel trace, every dispatch): {durs[0]:.2f}")
-    if xcd_cycles and "SQ_ACTIVE_INST_VALU" in mean:
+    if se_cycles and "SQ_ACTIVE_INST_VALU" in mean:
         # SQ_ACTIVE_INST_VALU counts issue quad-cycles (4 clocks) summed over waves
-        print(f"VALU_ISSUE_FRACTION: {4 * mean['SQ_ACTIVE_INST_VALU'] / (1024 * xcd_cycles):.3f}")
-    if xcd_cycles and "SQ_INSTS_MFMA" in mean:
+        print(f"VALU_ISSUE_FRACTION: {4 * mean['SQ_ACTIVE_INST_VALU'] / (1024 * se_cycles):.3f}")
+    if se_cycles and "SQ_INSTS_MFMA" in mean:
         per_simd = {c: mean[c] / 1024 for c in mean if c.startswith("SQ_INSTS")}
         print("INSTRUCTIONS_PER_SIMD_PER_DISPATCH: " +
               ", ".join(f"{c[9:]}={v:.4g}" for c, v in sorted(per_simd.items())))

@@ -62,3 +62,35 @@ def test_pins_and_abi_under_sanitizers(san_libs):
     print(out)
     assert r.returncode == 0, out
     assert "ERROR: AddressSanitizer" not in out and "runtime error" not in out, out
+
+
+def test_sanitizer_catches_planted_overflow(san_libs, tmp_path):
+    """The sanitizer run itself is pinned: a copy of the oracle whose P.V loop
+    runs one row too far (writing past O and reading past P on the last
+    head) must make the same child run fail with an AddressSanitizer
+    report."""
+    fa_lib, _ = san_libs
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    good = "for (long i = 0; i < N; ++i)\n            weighted_sum(P + i * N, vh, N, d, oh + i * d);"
+    assert src.count(good) == 1
+    bad_c = tmp_path / "oracle_overflow.c"
+    bad_c.write_text(src.replace(good, good.replace("i < N", "i <= N")))
+    bad_lib = str(tmp_path / "liboracle_overflow.so")
+    subprocess.run(["gcc", *SAN, "-std=c11", "-shared", "-fPIC", "-fopenmp", str(bad_c),
+                    "-o", bad_lib, "-lm"], check=True, capture_output=True, text=True)
+    env = dict(os.environ)
+    env.update({
+        "LD_PRELOAD": f"{_runtime('libasan.so')}:{_runtime('libubsan.so')}",
+        "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1:halt_on_error=1",
+        "SAN_FA_LIB": fa_lib, "SAN_ORACLE_LIB": bad_lib, "OMP_NUM_THREADS": "2",
+        "PYTHONPATH": ROOT + os.pathsep + env.get("PYTHONPATH", ""),
+    })
+    # -s: the report goes to the child's stderr, which pytest's own capture
+    # would swallow when the sanitizer aborts the process
+    cmd = [sys.executable, "-m", "pytest", "-q", "-x", "-s", "-p", "no:cacheprovider",
+           "-p", "tests.sanitize.plugin", "-m", "not gpu",
+           os.path.join(ROOT, "tests", "test_oracle_pins.py")]
+    r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    out = r.stdout + r.stderr
+    assert r.returncode != 0, out[-4000:]
+    assert "ERROR: AddressSanitizer" in out, out[-4000:]
