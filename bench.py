@@ -9,8 +9,9 @@ the MFMA-peak target is stated for).  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--pass fwd|bwd]
 
---pass decode times fa_decode (one step = the split kernel and the merge
-kernel) on a decode workload (default: the newest query over B=2, H=32,
+--pass decode times fa_decode (one step = one call: the split and merge
+kernels, or the single fused kernel for one or two queries over few chunks)
+on a decode workload (default: the newest query over B=2, H=32,
 Nk=8192, d=128): HBM-bound, so `value` and `roofline` are GB/s of compulsory
 traffic (read Q, K, V once, write O and LSE) against 8 TB/s.
 

@@ -15,6 +15,9 @@
 // kernel merges the chunks with the two-block rule of "解析 FlashAttention（2）"
 // (eq. (17)/(20) for the statistics, (37) for the output):
 //   LSE = ln sum_s e^(LSE_s),   O = sum_s e^(LSE_s - LSE) O_s.
+// With one or two queries and few chunks (many heads, short key axes) the
+// chunks of a head run as the waves of one workgroup instead and merge in
+// LDS, in one launch (decode_fused_kernel).
 //
 // With a handful of queries the work is a matrix-vector product: about Nq
 // FLOP per byte of K and V, far below the MFMA balance point, so the pass is
@@ -141,11 +144,17 @@ constexpr int kDecodeWaves = (NQ + 3) / 4;
 template <int DH>
 constexpr int kDecLayout = DH <= 64 ? 64 : 128;
 
+// The online-softmax state of one wave over keys [k0, k1) of head bh for
+// queries qbase .. qbase + NQW - 1 (NQW = min(NQ, 4)), merged over the
+// wave's RPW row groups: on return every lane holds its group's columns
+// col*8 .. +7 of the state (m, l, unnormalised acc), identical in all groups.
 template <typename E, int DH, int NQ, bool CAUSAL, bool STRIDED>
-__global__ void __launch_bounds__(64 * kDecodeWaves<NQ>)
-decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
-                    float *__restrict__ o_part, float *__restrict__ lse_part, int Nq, int Nk,
-                    int S, int chunk, float scale, float scale_log2, DecStrides st) {
+__device__ __forceinline__ void chunk_state(const E *__restrict__ Q, const E *__restrict__ K,
+                                            const E *__restrict__ V, int Nq, int Nk, int bh,
+                                            int k0, int k1, int qbase, float scale_log2,
+                                            const DecStrides &st, float (&m)[NQ < 4 ? NQ : 4],
+                                            float (&l)[NQ < 4 ? NQ : 4],
+                                            float (&acc)[NQ < 4 ? NQ : 4][8]) {
     constexpr int D = kDecLayout<DH>;
     constexpr int G = D / 8;       // lanes per key row
     constexpr int RPW = 64 / G;    // rows per load instruction
@@ -154,13 +163,8 @@ decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *_
     constexpr int BLK = RPW * ROUNDS;  // keys per block of loads
 
     const int lane = threadIdx.x & 63;
-    const int qbase = NQW * (threadIdx.x >> 6);  // first query of this wave
     const int grp = lane / G;
     const int col = lane % G;
-    const int s = blockIdx.x % S;
-    const int bh = blockIdx.x / S;
-    const int k0 = s * chunk;
-    const int k1 = min(Nk, k0 + chunk);
     const bool has_cols = DH == D || col * 8 < DH;  // this lane's columns exist
 
     // This lane's 8 columns of every query of the wave, widened to fp32.
@@ -178,7 +182,6 @@ decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *_
             qf[qi][2 * e + 1] = elem_hi<E>(w[e]);
         }
     }
-    float m[NQW], l[NQW], acc[NQW][8];
 #pragma unroll
     for (int qi = 0; qi < NQW; ++qi) {
         m[qi] = -INFINITY;
@@ -263,6 +266,30 @@ decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *_
         }
     }
 
+}
+
+template <typename E, int DH, int NQ, bool CAUSAL, bool STRIDED>
+__global__ void __launch_bounds__(64 * kDecodeWaves<NQ>)
+decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+                    float *__restrict__ o_part, float *__restrict__ lse_part, int Nq, int Nk,
+                    int S, int chunk, float scale, float scale_log2, DecStrides st) {
+    constexpr int D = kDecLayout<DH>;
+    constexpr int G = D / 8;              // lanes per key row
+    constexpr int NQW = NQ < 4 ? NQ : 4;  // queries per wave
+
+    const int lane = threadIdx.x & 63;
+    const int qbase = NQW * (threadIdx.x >> 6);  // first query of this wave
+    const int grp = lane / G;
+    const int col = lane % G;
+    const int s = blockIdx.x % S;
+    const int bh = blockIdx.x / S;
+    const int k0 = s * chunk;
+    const int k1 = min(Nk, k0 + chunk);
+    const bool has_cols = DH == D || col * 8 < DH;  // this lane's columns exist
+    float m[NQW], l[NQW], acc[NQW][8];
+    chunk_state<E, DH, NQ, CAUSAL, STRIDED>(Q, K, V, Nq, Nk, bh, k0, k1, qbase, scale_log2, st, m, l,
+                                            acc);
+
     if (grp == 0) {
 #pragma unroll
         for (int qi = 0; qi < NQW; ++qi) {
@@ -279,6 +306,75 @@ decode_split_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *_
             }
             if (col == 0) lse_part[prow] = l[qi] > 0.f ? m[qi] * scale + logf(l[qi]) : -INFINITY;
         }
+    }
+}
+
+// Split and merge in one launch, for one or two queries and at most
+// kFusedMaxChunks chunks: one workgroup per (batch, head) with one wave per
+// chunk.  Every wave leaves its chunk's unnormalised state (m, l, acc) in LDS,
+// and after a barrier the workgroup merges the S states with the same
+// two-block rule, O = sum_s 2^((m_s - M) c) acc_s / L with M = max_s m_s and
+// L = sum_s 2^((m_s - M) c) l_s, LSE = M scale + ln L (c = scale log2 e).  A
+// chunk in which a query sees no key has m = -inf and adds nothing; every
+// query sees at least one key (Nk >= Nq), so M is finite.  Saves the second
+// launch and the round trip of the partials through HBM where the heads are
+// many and the chunks few.
+template <int NQ>
+constexpr int kFusedMaxChunks = NQ == 1 ? 16 : 8;  // (register budget of the waves)
+
+template <typename E, int DH, int NQ, bool CAUSAL, bool STRIDED>
+__global__ void __launch_bounds__(64 * kFusedMaxChunks<NQ>)
+decode_fused_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
+                    E *__restrict__ O, float *__restrict__ LSE, int Nq, int Nk, int chunk,
+                    float scale, float scale_log2, DecStrides st) {
+    static_assert(NQ <= 2, "one wave per chunk holds all queries");
+    constexpr int D = kDecLayout<DH>;
+    constexpr int G = D / 8;
+    __shared__ float sm_acc[kFusedMaxChunks<NQ>][NQ][DH];
+    __shared__ float sm_m[kFusedMaxChunks<NQ>][NQ], sm_l[kFusedMaxChunks<NQ>][NQ];
+
+    const int lane = threadIdx.x & 63;
+    const int s = threadIdx.x >> 6;  // chunk of this wave
+    const int S = blockDim.x >> 6;
+    const int bh = blockIdx.x;
+    const int grp = lane / G;
+    const int col = lane % G;
+    const int k0 = s * chunk;
+    const int k1 = min(Nk, k0 + chunk);
+    float m[NQ], l[NQ], acc[NQ][8];
+    chunk_state<E, DH, NQ, CAUSAL, STRIDED>(Q, K, V, Nq, Nk, bh, k0, k1, 0, scale_log2, st, m, l,
+                                            acc);
+    if (grp == 0) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (qi >= Nq) break;
+            if (DH == D || col * 8 < DH) {
+#pragma unroll
+                for (int e = 0; e < 8; e += 4)
+                    *reinterpret_cast<float4 *>(&sm_acc[s][qi][col * 8 + e]) =
+                        make_float4(acc[qi][e], acc[qi][e + 1], acc[qi][e + 2], acc[qi][e + 3]);
+            }
+            if (col == 0) {
+                sm_m[s][qi] = m[qi];
+                sm_l[s][qi] = l[qi];
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int t = threadIdx.x; t < Nq * DH; t += blockDim.x) {
+        const int qi = t / DH, c = t - qi * DH;
+        float mx = sm_m[0][qi];
+        for (int u = 1; u < S; ++u) mx = fmaxf(mx, sm_m[u][qi]);
+        float lsum = 0.f, o = 0.f;
+        for (int u = 0; u < S; ++u) {
+            const float w = __builtin_amdgcn_exp2f((sm_m[u][qi] - mx) * scale_log2);
+            lsum = __builtin_fmaf(w, sm_l[u][qi], lsum);
+            o = __builtin_fmaf(w, sm_acc[u][qi][c], o);
+        }
+        O[dec_head_offset<DH, STRIDED>(st, bh, Nq, kDO) +
+          (size_t)qi * dec_row_stride<DH, STRIDED>(st, kDO) + c] = (E)(o / lsum);
+        if (c == 0) LSE[(size_t)bh * Nq + qi] = mx * scale + logf(lsum);
     }
 }
 
@@ -665,6 +761,14 @@ hipError_t launch_nq(const void *q, const void *k, const void *v, void *o, float
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     const E *Q = static_cast<const E *>(q), *K = static_cast<const E *>(k),
             *V = static_cast<const E *>(v);
+    if constexpr (NQ <= kDecodeValuQueries) {
+        if (S <= kFusedMaxChunks<NQ>) {
+            hipLaunchKernelGGL((decode_fused_kernel<E, DH, NQ, CAUSAL, STRIDED>), dim3(B * H),
+                               dim3(64 * S), 0, stream, Q, K, V, static_cast<E *>(o), lse, Nq, Nk,
+                               chunk, scale, scale_log2, st);
+            return hipGetLastError();
+        }
+    }
     if constexpr (NQ > kDecodeValuQueries)
         hipLaunchKernelGGL((decode_mfma_kernel<E, DH, CAUSAL, STRIDED>), dim3(B * H * S), dim3(64),
                            0, stream, Q, K, V, o_part, lse_part, Nq, Nk, S, chunk, scale,

@@ -164,8 +164,10 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
  * Scores, statistics and sums are fp32.  Shapes: B, H >= 1, 1 <= Nq <= 16,
  * Nq <= Nk <= 2^30, d a multiple of 16 up to 128, B*H*Nk*d < 2^40,
  * B*H*ceil(Nk/128) <= 2^22 and B*H*Nq <= 2^22 (launch-size limits).  Two
- * kernels are enqueued on `stream`.  Errors as for fa_fwd, plus
- * FA_ERR_WORKSPACE.
+ * kernels (chunks, then merge) are enqueued on `stream`; one query over at
+ * most 16 chunks, or two over at most 8, run chunks and merge in a single
+ * kernel (one workgroup per head, merging in LDS) and leave the workspace
+ * untouched.  Errors as for fa_fwd, plus FA_ERR_WORKSPACE.
  */
 int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int Nq, int Nk, int d, float scale, int causal,

@@ -60,6 +60,14 @@ CASES = [
     (2, 2, 12, 511, 128, False, "uniform", 2),
     (1, 3, 7, 4096, 64, True, "normal", 0),
     (1, 2, 9, 200, 64, True, "normal", 4),
+    # one or two queries and at most eight chunks run split and merge in one
+    # workgroup per head (one wave per chunk); more chunks take the split and
+    # merge kernels
+    (2, 3, 2, 449, 128, True, "normal4", 8),   # last chunk: one key, hidden from query 0
+    (1, 2, 2, 300, 80, True, "uniform", 0),
+    (3, 5, 1, 511, 48, False, "normal", 0),
+    (1, 2, 2, 1500, 128, True, "normal", 0),   # 24 chunks: split and merge kernels
+    (1, 1, 1, 700, 64, False, "normal4", 9),   # 9 requested: 11 keys over 64 each -> 9 chunks
 ]
 
 
@@ -84,14 +92,17 @@ def test_decode_workloads(name, oracle_lib):
     check(o, lse, o_ref, lse_ref, w.name)
 
 
-def test_decode_split_counts_agree(oracle_lib):
-    """Any split of the key axis gives the same result within rounding."""
-    w = inputs.DecodeWorkload("splits", 1, 4, 4, 5000, 128, "normal", True, seed=44)
+@pytest.mark.parametrize("nq", [1, 2, 4])
+def test_decode_split_counts_agree(nq, oracle_lib):
+    """Any split of the key axis gives the same result within rounding (with
+    one or two queries, up to eight chunks merge inside one workgroup and
+    more in the merge kernel)."""
+    w = inputs.DecodeWorkload("splits", 1, 4, nq, 5000, 128, "normal", True, seed=44 + nq)
     q, k, v = inputs.make_decode_qkv(w)
     o_ref, lse_ref = oracle_lib.attention_qk(q, k, v, w.scale, True)
-    for splits in (1, 2, 7, 40, 79, 0):
+    for splits in (1, 2, 7, 8, 9, 40, 79, 0):
         o, lse = run_decode(q, k, v, True, w.scale, splits)
-        check(o, lse, o_ref, lse_ref, f"splits={splits}")
+        check(o, lse, o_ref, lse_ref, f"nq={nq} splits={splits}")
 
 
 def test_decode_equals_forward_rows():

@@ -50,9 +50,10 @@ def _bnhd(t):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("nq,d", [(1, 128), (2, 64), (5, 128), (16, 80)])
-def test_strided_matches_dense(dtype, nq, d):
-    w = inputs.DecodeWorkload(f"decst_{dtype}_{nq}_{d}", 2, 3, nq, 1500, d, "normal", True,
+@pytest.mark.parametrize("nq,d,nk", [(1, 128, 1500), (2, 64, 1500), (5, 128, 1500),
+                                     (16, 80, 1500), (1, 96, 300), (2, 128, 500)])
+def test_strided_matches_dense(dtype, nq, d, nk):
+    w = inputs.DecodeWorkload(f"decst_{dtype}_{nq}_{d}_{nk}", 2, 3, nq, nk, d, "normal", True,
                               seed=28000 + nq + d, dtype=dtype)
     q, k, v = (t.cuda() for t in inputs.make_decode_qkv(w))
     o, lse = fa.decode(q, k, v, causal=True, scale=w.scale)
