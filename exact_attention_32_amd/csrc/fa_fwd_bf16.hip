@@ -625,8 +625,14 @@ fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict
                             pop[2 * kb + 1] = __builtin_convertvector(hi, X8);
                         }
                     };
-                    exps(mc_run);
-                    if (__ballot(!(rs <= kSumMax<E>))) {
+                    // The first tile of a work item (t = 0) always takes the slow
+                    // path (the base is still -inf), so it skips the attempt.
+                    bool slow = t == 0;
+                    if (!slow) {
+                        exps(mc_run);
+                        slow = __ballot(!(rs <= kSumMax<E>)) != 0;
+                    }
+                    if (slow) {
                         // Slow path: the base moves to the row maximum (tile and
                         // running), the accumulator and sum are rescaled, and the
                         // tile's probabilities are recomputed against the new base.
@@ -1190,21 +1196,6 @@ constexpr int kPipeWaves = 8;
 constexpr int kPipeWaves64 = 4;
 constexpr int kPipeMinN64 = 8192;
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // Schedule of a forward launch with `slots` persistent workgroup slots (see
 // sched_item): mode 2 when the heads and slots split evenly over the XCDs and,
 // under the causal mask, the rounds pair up; tile pairs (mode 1) when there
@@ -1334,6 +1325,21 @@ hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float 
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int N, int d, float scale, bool causal,

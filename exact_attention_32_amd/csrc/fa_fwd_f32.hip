@@ -4,16 +4,21 @@
 // Same operation and the same online-softmax recurrence as the bf16 kernel
 // (page "解析 FlashAttention（2）", eq. (17), (20), (36)-(37), unnormalised
 // form with one division at the end), on the vector ALUs.  A workgroup takes
-// R query rows and splits their key axis over S = 16 thread groups: thread
+// R query rows and splits their key axis over S thread groups: thread
 // (r, s) owns query row r and, in every 64-key tile staged in LDS, the keys
-// s, s + 16, s + 32, s + 48; it keeps q, its own (m, l) and an unnormalised
-// fp32 accumulator in registers.  At the end the S partial results of a row
-// are merged through LDS by the two-block rule of eq. (17)/(20) (each
-// partial weighted by e^{m_s - m}), each thread producing D/S columns of
-// the output.  Splitting the keys puts 16 threads on every query row, so
-// small problems spread over many more lanes than one thread per row would.
-// This path serves fp32 callers and small problems; it is not a tuned
-// hot path.
+// s, s + S, ...; it keeps q, its own (m, l) and an unnormalised fp32
+// accumulator in registers.  At the end the S partial results of a row are
+// merged through LDS by the two-block rule of eq. (17)/(20) (each partial
+// weighted by e^{m_s - m}), each thread producing D/S columns of the output.
+// Splitting the keys puts S threads on every query row, so small problems
+// spread over many more lanes than one thread per row would.  Two shapes of
+// workgroup: R = 16 (8 above d = 64) rows and S = 16, and for grids that
+// would leave compute units idle a quarter of the rows and S = 64 (four
+// times the workgroups, a quarter of the keys per thread).  The S threads
+// of a row are consecutive lanes, so a 16-lane pass of an LDS read fetches
+// 16 different key rows (the pitch puts them in distinct banks) instead of
+// broadcasting one.  This path serves fp32 callers and small problems; it
+// is not a tuned hot path.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -23,39 +28,38 @@
 namespace fa {
 namespace {
 
-constexpr int kSplit = 16;                  // key groups per query row
-constexpr int kPerTile = 4;                 // keys per thread and tile
-constexpr int kTileKeys = kSplit * kPerTile;  // keys per LDS tile
-// Query rows per workgroup: 16 (256 threads) up to d = 64, 8 (128 threads)
-// above, where q and the accumulator take 2d registers per thread.
+constexpr int kTileKeys = 64;  // keys per LDS tile
+// Query rows per workgroup of the default shape (S = 16): 16 (256 threads)
+// up to d = 64, 8 (128 threads) above, where q and the accumulator take 2d
+// registers per thread.
 template <int D>
 constexpr int kRowsF = D <= 64 ? 16 : 8;
-// LDS row pitch in floats: 4 more than d, so that the four key rows a wave
-// reads at once start in different banks.
+// LDS row pitch in floats: 4 more than d, so that consecutive key rows start
+// four banks apart.
 template <int D>
 constexpr int kPitch = D + 4;
 // Floats of the shared array: the K and V tiles while the keys stream, then
 // the partial results (acc, m, l) of every thread for the merge.
-template <int D>
-constexpr int kSharedFloats = 2 * kTileKeys * kPitch<D> > kRowsF<D> * kSplit * (D + 2)
+template <int D, int R, int S>
+constexpr int kSharedFloats = 2 * kTileKeys * kPitch<D> > R * S * (D + 2)
                                   ? 2 * kTileKeys * kPitch<D>
-                                  : kRowsF<D> * kSplit * (D + 2);
+                                  : R * S * (D + 2);
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kRowsF<D> * kSplit)
+template <int D, int R, int kSplit, bool CAUSAL>
+__global__ void __launch_bounds__(R * kSplit)
 fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
                const float *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE,
                int N, int nqt, float scale, float scale_log2) {
-    constexpr int R = kRowsF<D>;
+    constexpr int kPerTile = kTileKeys / kSplit;  // keys per thread and tile
     constexpr int P = kPitch<D>;
     constexpr int kThreadsF = R * kSplit;
-    __shared__ __attribute__((aligned(16))) float sh[kSharedFloats<D>];
+    __shared__ __attribute__((aligned(16))) float sh[kSharedFloats<D, R, kSplit>];
     float *const ks = sh;                    // [kTileKeys][P]
     float *const vs = sh + kTileKeys * P;    // [kTileKeys][P]
 
     const int tid = threadIdx.x;
-    const int r = tid % R;
-    const int sg = tid / R;
+    const int r = tid / kSplit;
+    const int sg = tid % kSplit;
     const int bh = blockIdx.x / nqt;
     const int qt = blockIdx.x - bh * nqt;
     const int r0 = qt * R;
@@ -128,7 +132,7 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
             if (c0 + kTileKeys < kv_end) fetch(c0 + kTileKeys);
         }
 
-        // Scores of this thread's keys c0 + sg + 16j, masked keys -inf.
+        // Scores of this thread's keys c0 + sg + kSplit j, masked keys -inf.
         float s[kPerTile];
         float mt = -INFINITY;
 #pragma unroll
@@ -213,14 +217,29 @@ fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
     }
 }
 
+template <int D, int R, int S, bool CAUSAL>
+hipError_t launch_rs(const float *q, const float *k, const float *v, float *o, float *lse, int B,
+                     int H, int N, float scale, hipStream_t stream) {
+    const int nqt = (N + R - 1) / R;
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, R, S, CAUSAL>), dim3(B * H * nqt), dim3(R * S), 0,
+                       stream, q, k, v, o, lse, N, nqt, scale, scale_log2);
+    return hipGetLastError();
+}
+
+// The default shape, unless its grid has fewer workgroups than the device
+// has compute units: then four times as many workgroups of a quarter of the
+// rows, each row's keys split 64 ways (w1's B1 H1 N256 d64: 9.1 instead of
+// 14.8 us; from about two workgroups per compute unit on the default shape
+// is faster).
 template <int D, bool CAUSAL>
 hipError_t launch(const float *q, const float *k, const float *v, float *o, float *lse, int B,
                   int H, int N, float scale, hipStream_t stream) {
-    const int nqt = (N + kRowsF<D> - 1) / kRowsF<D>;
-    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(B * H * nqt), dim3(kRowsF<D> * kSplit),
-                       0, stream, q, k, v, o, lse, N, nqt, scale, scale_log2);
-    return hipGetLastError();
+    constexpr int R = kRowsF<D>;
+    const long wgs = (long)B * H * ((N + R - 1) / R);
+    if (wgs < device_cus())
+        return launch_rs<D, R / 4, 64, CAUSAL>(q, k, v, o, lse, B, H, N, scale, stream);
+    return launch_rs<D, R, 16, CAUSAL>(q, k, v, o, lse, B, H, N, scale, stream);
 }
 
 }  // namespace

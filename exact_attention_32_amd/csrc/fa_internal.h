@@ -22,6 +22,10 @@ namespace fa {
 
 constexpr bool kSafeSync = FA_SAFE_SYNC != 0;
 
+// Compute units of the current device (looked up once per device; 256 if
+// the runtime cannot say).
+int device_cus();
+
 // Each launcher enqueues one kernel on `stream` and returns the launch status
 // (hipGetLastError).  Arguments have already been validated by fa_api.cpp.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,

@@ -163,6 +163,12 @@ SMALL = [
     (1, 2, 100, 64, "f32", "normal", True),
     (2, 1, 300, 128, "f32", "normal", False),
     (1, 2, 257, 128, "f32", "uniform", True),
+    # fp32 grids of at least one workgroup per compute unit (on 256 compute
+    # units) take the 16-row (8 above d = 64), 16-way key split; the smaller
+    # ones above a quarter of the rows with a 64-way split
+    (2, 8, 300, 64, "f32", "normal", True),
+    (4, 8, 130, 128, "f32", "uniform", False),
+    (1, 16, 257, 48, "f32", "normal", True),
 ]
 
 
