@@ -73,9 +73,12 @@ def test_backward_graph_replays():
             assert torch.equal(a, b), f"replay {i}"
 
 
-@pytest.mark.parametrize("nq", [1, 4])
-def test_decode_graph_replays(nq):
-    dw = inputs.DecodeWorkload(f"graph_dec{nq}", 2, 4, nq, 3000, 128, "normal", True, seed=33000 + nq)
+# (1, 3000) and (4, 3000): split and merge kernels; (1, 600) and (2, 400):
+# few chunks, split and merge in one kernel
+@pytest.mark.parametrize("nq,nk", [(1, 3000), (4, 3000), (1, 600), (2, 400)])
+def test_decode_graph_replays(nq, nk):
+    dw = inputs.DecodeWorkload(f"graph_dec{nq}_{nk}", 2, 4, nq, nk, 128, "normal", True,
+                               seed=33000 + nq)
     q0, k0, v0 = (t.cuda() for t in inputs.make_decode_qkv(dw))
     q, k, v = q0.clone(), k0.clone(), v0.clone()
     g, (o, lse) = _capture(lambda: fa.decode(q, k, v, causal=True, scale=dw.scale))

@@ -98,7 +98,7 @@ def test_backward_checking_build_identical(B, H, N, d, causal, libs):
 
 
 @pytest.mark.parametrize("Nq,Nk,d,causal", [(1, 5000, 128, False), (8, 3000, 64, True),
-                                             (16, 4097, 128, True)])
+                                             (16, 4097, 128, True), (2, 500, 64, True)])
 def test_decode_checking_build_identical(Nq, Nk, d, causal, libs):
     reg, safe = libs
     w = inputs.DecodeWorkload(f"syncd_{Nq}x{Nk}x{d}", 2, 3, Nq, Nk, d, "normal", causal, 900 + Nk)
