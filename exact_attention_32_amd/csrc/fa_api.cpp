@@ -284,7 +284,7 @@ int fa_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, float 
 
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
     if (!decode_shape_ok(B, H, Nq, Nk, d)) return 0;
-    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    const int S = fa::decode_num_splits(B, H, Nq, Nk, num_splits);
     return (size_t)decode_workspace(B, H, Nq, d, S, nullptr);
 }
 
@@ -297,7 +297,7 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
     if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
-    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    const int S = fa::decode_num_splits(B, H, Nq, Nk, num_splits);
     uint64_t lse_off = 0;
     const uint64_t need = decode_workspace(B, H, Nq, d, S, &lse_off);
     if (!workspace || (uint64_t)workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -331,7 +331,7 @@ int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, floa
     if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
     if (!decode_shape_ok(B, H, Nq, Nk, d)) return FA_ERR_SHAPE;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
-    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    const int S = fa::decode_num_splits(B, H, Nq, Nk, num_splits);
     uint64_t lse_off = 0;
     const uint64_t need = decode_workspace(B, H, Nq, d, S, &lse_off);
     if (need > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
@@ -372,7 +372,7 @@ int fa_decode_ex(int dtype, const void *q, const void *k, const void *v, void *o
         if (st[0] < 0 || st[1] < 0 || st[2] < d || st[2] > (1 << 24)) return FA_ERR_STRIDE;
         if (st[0] > (int64_t)1 << 50 || st[1] > (int64_t)1 << 50) return FA_ERR_STRIDE;
     }
-    const int S = fa::decode_num_splits(B, H, Nk, num_splits);
+    const int S = fa::decode_num_splits(B, H, Nq, Nk, num_splits);
     uint64_t lse_off = 0;
     const uint64_t need = decode_workspace(B, H, Nq, d, S, &lse_off);
     if (!workspace || (uint64_t)workspace_bytes < need) return FA_ERR_WORKSPACE;

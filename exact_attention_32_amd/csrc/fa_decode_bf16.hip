@@ -395,8 +395,7 @@ decode_fused_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *_
 // for its own reads of a buffer (lgkmcnt) before refilling it.  LDS layout
 // and read offsets: the shared swizzle of fa_tiles.h (conflict-free for
 // both read patterns).
-constexpr int kDecodeValuQueries = 2;  // at most this many queries: VALU kernel
-constexpr int kDecTile = 32;           // keys per LDS tile
+constexpr int kDecTile = 32;  // keys per LDS tile
 // Largest half-row probability sum accepted against the current exponent
 // base (every probability of the tile is then at most this): 2^32 for bf16
 // probabilities, 2^15 for fp16 ones (largest finite value 65504).
@@ -803,7 +802,10 @@ template <typename E, bool STRIDED>
 hipError_t launch_e(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                     int H, int Nq, int Nk, int d, float scale, bool causal, int S, float *o_part,
                     float *lse_part, const DecStrides &st, hipStream_t stream) {
-    const int chunk = decode_chunk(Nk, S);
+    // The MFMA kernel walks its chunk in rounds of three 32-key tiles, so its
+    // chunks are whole rounds (a chunk of 256 keys would run 9 tile slots for
+    // 8 tiles); the vector-ALU kernels take whole 64-key blocks.
+    const int chunk = decode_chunk(Nk, S, Nq > kDecodeValuQueries ? 3 * kDecTile : 64);
     S = (Nk + chunk - 1) / chunk;  // no empty chunk
 #define FA_DEC_CASE(DH)                                                                         \
     case DH:                                                                                    \

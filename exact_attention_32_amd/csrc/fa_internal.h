@@ -75,12 +75,25 @@ constexpr int kMaxDevices = 64;
 // Device address of the current device's copy of that scratch (looked up
 // once per device with hipGetSymbolAddress).
 hipError_t decode_scratch(void **ptr);
-constexpr int kDecodeMinChunk = 64;       // keys per chunk, at least
-constexpr int kDecodeTargetWaves = 2048;  // single-wave workgroups aimed for
+constexpr int kDecodeMinChunk = 64;  // keys per chunk, at least
+// At most this many queries run on the vector-ALU kernels, more on the MFMA
+// kernel.
+constexpr int kDecodeValuQueries = 2;
+// Single-wave workgroups aimed for by the automatic split count (sized for
+// 256 compute units): the vector-ALU kernels, 8 per compute unit; the MFMA
+// kernel, whose three 16 KiB tile buffers per wave leave room for three
+// waves per compute unit at d = 128, one round of them (a second, partial
+// round of waves costs more than the longer chunks: B2 H32 Nq16 Nk8192 d128
+// causal 47 us at 704 waves against 54-56 us at 960-2048).
+constexpr int kDecodeTargetWaves = 2048;
+constexpr int kDecodeTargetWavesMfma = 768;
 // Number of chunks for a requested count (<= 0: automatic).
-int decode_num_splits(int B, int H, int Nk, int requested);
-// Keys per chunk for S chunks (a multiple of 64).
-int decode_chunk(int Nk, int S);
+int decode_num_splits(int B, int H, int Nq, int Nk, int requested);
+// Keys per chunk for S chunks: the least multiple of `granule` that covers
+// Nk in S chunks (the kernels' unit of work: 64 keys for the vector-ALU
+// kernels, whole blocks of loads at both head dims; 96 for the MFMA kernel,
+// one round of three 32-key tiles).
+int decode_chunk(int Nk, int S, int granule);
 // Enqueues the split kernel (partials into o_part [B,H,S,Nq,d] and lse_part
 // [B,H,S,Nq], fp32) and the merge kernel.
 hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -7,22 +7,22 @@
 
 namespace fa {
 
-int decode_num_splits(int B, int H, int Nk, int requested) {
+int decode_num_splits(int B, int H, int Nq, int Nk, int requested) {
     const long smax = (Nk + kDecodeMinChunk - 1) / kDecodeMinChunk;
     if (requested > 0) return (int)std::min<long>(requested, smax);
-    // About kDecodeTargetWaves single-wave workgroups in all, chunks of at
+    // About the target number of single-wave workgroups in all, chunks of at
     // least kDecodeMinChunk keys.
+    const long target = Nq > kDecodeValuQueries ? kDecodeTargetWavesMfma : kDecodeTargetWaves;
     const long bh = (long)B * H;
-    long s = (kDecodeTargetWaves + bh - 1) / bh;
+    long s = (target + bh - 1) / bh;
     if (s > smax) s = smax;
     if (s < 1) s = 1;
     return (int)s;
 }
 
-int decode_chunk(int Nk, int S) {
-    // a multiple of 64 keys (whole blocks of loads at both head dims)
+int decode_chunk(int Nk, int S, int granule) {
     const int c = (Nk + S - 1) / S;
-    return (c + 63) / 64 * 64;
+    return (c + granule - 1) / granule * granule;
 }
 
 }  // namespace fa

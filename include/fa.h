@@ -156,8 +156,11 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
  *   o         : bf16 [B, H, Nq, d], written (rounded to nearest even)
  *   lse       : fp32 [B, H, Nq], written (natural log, as fa_fwd)
  *   num_splits: chunks of the key axis; <= 0 chooses automatically (about
- *               2048 chunks over all heads, at least 64 keys each); a larger
- *               request is cut to ceil(Nk / 64)
+ *               2048 chunks over all heads for one or two queries, 768 for
+ *               more, at least 64 keys each); a larger request is cut to
+ *               ceil(Nk / 64).  Chunks are whole multiples of 64 keys (96
+ *               for three or more queries), so fewer chunks than asked for
+ *               may run.
  *   workspace : device memory of at least fa_decode_workspace_size(...)
  *               bytes for the fp32 partials; its contents on return are
  *               unspecified; it must not overlap any other argument
