@@ -177,6 +177,16 @@ def test_decode_workspace_size(lib):
                 (1, 1, 8, 7, 64, 0), (1, 1, 1, 100, 72, 0), (1, 1, 1, 100, 144, 0)):
         assert ws(*bad) == 0, bad
     assert ws(1, 1, 1, 100, 96, 1) >= 96 * 4 + 4   # every multiple of 16 up to 128
+    # automatic split count: about 2048 single-wave workgroups for one or two
+    # queries (vector-ALU kernels), 768 for more (MFMA kernel), at least 64
+    # keys per chunk
+    for B, H, Nq, Nk, d, S in ((2, 32, 1, 8192, 128, 32), (2, 32, 2, 8192, 64, 32),
+                               (2, 32, 3, 8192, 128, 12), (2, 32, 16, 8192, 128, 12),
+                               (1, 16, 1, 16384, 64, 128), (1, 8, 16, 32768, 128, 96),
+                               (16, 12, 1, 1000, 64, 11), (16, 12, 4, 1000, 64, 4),
+                               (1, 1, 16, 300, 128, 5), (64, 64, 8, 8192, 128, 1)):
+        assert ws(B, H, Nq, Nk, d, 0) == ws(B, H, Nq, Nk, d, S), (B, H, Nq, Nk, d, S)
+        assert ws(B, H, Nq, Nk, d, 0) < ws(B, H, Nq, Nk, d, S + 1) or S * 64 >= Nk
 
 
 def test_decode_validation_codes(lib):
