@@ -1,7 +1,7 @@
 """fa_decode_noalloc (the allocation-free decode: partials in the library's
 fixed device scratch instead of a caller workspace) against fa_decode, the
-entry point it is a variant of: on two calls in a row, the second with a
-smaller input (so the scratch still holds the first call's partials), the
+entry point it is a variant of: on calls in a row, each with a smaller
+input than the one before (so the scratch still holds older partials), the
 outputs must equal fa_decode's with the same num_splits bit for bit (same
 kernels, same split), and both must meet the fp64 oracle's bf16 gates."""
 import numpy as np
@@ -14,8 +14,12 @@ from exact_attention_32_amd import inputs
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (B, H, Nq, Nk, d, causal, splits, seed): the second call is the smaller one
+    # (B, H, Nq, Nk, d, causal, splits, seed), each call smaller than the one
+    # before: MFMA split kernel and merge, vector-ALU split kernel and merge
+    # (partials in the scratch again), then split and merge in one kernel
+    # (no partials at all)
     (2, 8, 4, 6000, 128, True, 0, 61),
+    (1, 2, 1, 3000, 128, True, 0, 63),
     (1, 4, 1, 1000, 64, False, 0, 62),
 ]
 
@@ -36,7 +40,7 @@ def _run(fn_name, w, q, k, v, splits):
     return o, lse
 
 
-def test_noalloc_matches_fa_decode_on_two_calls(oracle_lib):
+def test_noalloc_matches_fa_decode_on_calls_in_a_row(oracle_lib):
     for B, H, Nq, Nk, d, causal, splits, seed in CASES:
         w = inputs.DecodeWorkload(f"noalloc_{B}x{H}x{Nq}x{Nk}x{d}", B, H, Nq, Nk, d, "normal",
                                   causal, seed)
