@@ -68,6 +68,10 @@ CASES = [
     (3, 5, 1, 511, 48, False, "normal", 0),
     (1, 2, 2, 1500, 128, True, "normal", 0),   # 24 chunks: split and merge kernels
     (1, 1, 1, 700, 64, False, "normal4", 9),   # 9 requested: 11 keys over 64 each -> 9 chunks
+    # more chunks than the merge kernel stages at once (1024): its weights
+    # go through LDS in several passes
+    (1, 1, 1, 131072, 64, False, "normal", 2048),
+    (1, 2, 3, 120000, 128, True, "normal4", 1300),   # MFMA kernel: 1250 chunks of 96 keys
 ]
 
 
