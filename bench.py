@@ -59,7 +59,6 @@ import argparse
 import glob
 import hashlib
 import json
-import math
 import os
 import sys
 import time

@@ -2,7 +2,6 @@
 include/fa.h declares, and rejects bad arguments with the documented codes
 before anything reaches the GPU (every call here fails validation, so no HIP
 runtime call is made)."""
-import ctypes
 import os
 import re
 
