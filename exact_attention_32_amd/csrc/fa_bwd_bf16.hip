@@ -48,7 +48,8 @@ namespace {
 // dq kernel: one workgroup = 128 queries of one (batch, head); wave w owns
 // queries r0 + 32w .. +31 (lane (g, j) holds query j of the wave).
 // ---------------------------------------------------------------------------
-// Both kernels run two waves per SIMD (<= 256 registers per lane).  The
+// Both kernels run two waves per SIMD (<= 256 registers per lane), but for
+// the d = 64 dq kernel on shorter rows (three, see the launcher).  The
 // dkdv kernel holds K, V and two accumulators in registers (192 of them at
 // d = 128); there its two 32-query halves run as a loop, not unrolled, which
 // keeps their live ranges apart (a few registers still go to scratch, which
@@ -64,6 +65,8 @@ template <int D>
 constexpr int kDqWaves = 2;
 template <int D>
 constexpr int kDkdvWaves = 2;
+// Rows shorter than this run the d = 64 dq kernel at three waves per SIMD.
+constexpr int kDq3MaxN = 8192;
 
 // Element strides (batch, head, row) of the eight [B, H, N, d] tensors, d
 // contiguous, in the order of the enum below; LSE and delta stay dense
@@ -92,9 +95,9 @@ __device__ __forceinline__ int row_stride(const BwdStrides &st, int t) {
     else return DH;
 }
 
-template <typename E, int DH, bool CAUSAL, bool STRIDED>
+template <typename E, int DH, bool CAUSAL, bool STRIDED, int OCC = kDqWaves<kLayout<DH>>>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kDqWaves<kLayout<DH>>, kDqWaves<kLayout<DH>>)))
+__attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V,
               const E *__restrict__ O, const E *__restrict__ dO, const float *__restrict__ LSE,
               float *__restrict__ Delta, E *__restrict__ dQ, int N, int ntiles, float scale,
@@ -560,9 +563,22 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
     const E *Q = static_cast<const E *>(q), *K = static_cast<const E *>(k),
             *V = static_cast<const E *>(v), *O = static_cast<const E *>(o),
             *dO = static_cast<const E *>(dout);
-    hipLaunchKernelGGL((bwd_dq_kernel<E, DH, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads), 0,
-                       stream, Q, K, V, O, dO, lse, delta, static_cast<E *>(dq), N, ntiles, scale,
-                       scale_log2, st);
+    // At d = 64 the dq kernel fits three waves per SIMD (165 registers);
+    // that measured 2-2.5 % faster on rows up to a few thousand keys (B4 H16
+    // N2048, B16 H12 N1000, both masks) and 1.2 % slower on B1 H16 N16384
+    // causal, so long rows keep two.
+    bool three = false;
+    if constexpr (DH == 64) {
+        three = N < kDq3MaxN;
+        if (three)
+            hipLaunchKernelGGL((bwd_dq_kernel<E, DH, CAUSAL, STRIDED, 3>), dim3(blocks),
+                               dim3(kThreads), 0, stream, Q, K, V, O, dO, lse, delta,
+                               static_cast<E *>(dq), N, ntiles, scale, scale_log2, st);
+    }
+    if (!three)
+        hipLaunchKernelGGL((bwd_dq_kernel<E, DH, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads),
+                           0, stream, Q, K, V, O, dO, lse, delta, static_cast<E *>(dq), N, ntiles,
+                           scale, scale_log2, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, DH, CAUSAL, STRIDED>), dim3(blocks), dim3(kThreads), 0,
