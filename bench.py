@@ -27,9 +27,9 @@ dq kernel and the dkdv kernel) with the nominal backward FLOPs
 10*B*H*N^2*d (five N x N x d products), halved under the causal mask.
 
 FLOPs are the nominal matmul count 4*B*H*N^2*d, halved under the causal
-mask.  `roofline` reports the kernel's own average launch duration, measured
-with HIP events recorded on the launch stream, against the bf16 dense MFMA
-peak; `traffic` comes from the committed rocprofv3 counter summary of the
+mask.  `roofline` reports the average launch duration, measured with one
+pair of HIP events recorded on the launch stream around the K timed steps
+(`kernel_ms`), against the bf16 dense MFMA peak; `traffic` comes from the committed rocprofv3 counter summary of the
 same command when it still matches the kernel source.  `cpu_baseline` times
 the fp64 oracle on a bounded sample of rows of the same workload.
 
@@ -77,6 +77,30 @@ KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_fwd_bf16.hip",
                   "exact_attention_32_amd/csrc/fa_fwd_f32.hip"]
 BWD_KERNEL_SOURCES = ["exact_attention_32_amd/csrc/fa_bwd_bf16.hip"]
 COPY_BYTES = 1 << 30
+
+
+def run_timed(step, stream, dev, steps: int):
+    """The timed region: `steps` steps back to back on `stream`, synchronised
+    on both sides.  Returns (wall seconds, mean milliseconds per step between
+    one pair of HIP events recorded on the launch stream around the steps).
+    The mean includes the dispatch gap between consecutive launches.  An
+    event pair around every step would lengthen every step instead: the
+    extra markers between launches measured 26 us per step at B2 H32 N8192
+    d128 (1010 vs 978 us) and 5-8 us on launches of 10-50 us."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / steps
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -375,19 +399,7 @@ def bench_decode(args) -> int:
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             step()
-    torch.cuda.synchronize(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for a, b in evs:
-            a.record(stream)
-            step()
-            b.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    kernel_ms = sum(launch_ms) / len(launch_ms)
+    wall, kernel_ms = run_timed(step, stream, dev, args.steps)
     ms_per_step = wall * 1e3 / args.steps
     gbs = w.bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
@@ -410,9 +422,7 @@ def bench_decode(args) -> int:
                    "tflops": round(w.flops / (kernel_ms * 1e-3) / 1e12, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "kernel_ms": round(kernel_ms, 4),
-                     "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
-                     "kernel_ms_min": round(launch_ms[0], 4)},
+                     "traffic": None, "kernel_ms": round(kernel_ms, 4)},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -651,21 +661,9 @@ def main() -> int:
             step()
     torch.cuda.synchronize(dev)
 
-    # Timed region: K steps, synchronised on both sides.  Per-launch event
-    # pairs on the launch stream give the kernel's average duration.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for a, b in evs:
-            a.record(stream)
-            step()
-            b.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    kernel_ms = sum(launch_ms) / len(launch_ms)
+    # Timed region: K steps, synchronised on both sides; one event pair on
+    # the launch stream around them gives the average launch duration.
+    wall, kernel_ms = run_timed(step, stream, dev, args.steps)
     ms_per_step = wall * 1e3 / args.steps
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -677,17 +675,13 @@ def main() -> int:
                 "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": read_traffic(w.name) if args.which == "fwd" else None,
-                "kernel_ms": round(kernel_ms, 4),
-                "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
-                "kernel_ms_min": round(launch_ms[0], 4)}
+                "kernel_ms": round(kernel_ms, 4)}
     if args.which == "kvouter":
         nbytes = kvouter_bytes(w)
         gbs = nbytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                    "kernel_ms": round(kernel_ms, 4),
-                    "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
-                    "kernel_ms_min": round(launch_ms[0], 4), "algorithmic_bytes": nbytes}
+                    "kernel_ms": round(kernel_ms, 4), "algorithmic_bytes": nbytes}
     if args.which == "bwd":
         metric = "attention bwd TFLOP/s on 1 MI355X (bf16, causal/non-causal) + % MFMA peak"
     line = {
